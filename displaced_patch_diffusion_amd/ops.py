@@ -1,0 +1,139 @@
+"""Python binding of libdp: one function per C entry point, same names.
+
+Argument marshalling only: tensors must already be contiguous device tensors
+of the right dtype; every step runs in libdp's HIP kernels on torch's current
+stream.  Outputs and workspaces are allocated here with torch when the caller
+does not pass them.
+"""
+from __future__ import annotations
+
+import torch
+
+from ._lib import DP_BF16, DP_F32, check, lib
+
+_DT = {torch.bfloat16: DP_BF16, torch.float32: DP_F32}
+
+
+def _dt(*ts) -> int:
+    dts = {t.dtype for t in ts if t is not None}
+    if len(dts) != 1 or next(iter(dts)) not in _DT:
+        raise TypeError(f"expected one of bf16/f32 for all tensors, got {dts}")
+    return _DT[dts.pop()]
+
+
+def _dev(*ts, f32=()):
+    for t in ts:
+        if t is None:
+            continue
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("tensors must be contiguous and on the GPU")
+    for t in f32:
+        if t is not None and (t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous()):
+            raise ValueError("statistics, gamma/beta and bias must be contiguous float32 GPU tensors")
+
+
+def _p(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _ws(nbytes: int, device) -> torch.Tensor | None:
+    return torch.empty(nbytes, dtype=torch.uint8, device=device) if nbytes else None
+
+
+def dp_kv_buffer_splice(k_buf, v_buf, k_fresh, v_fresh, t0: int) -> None:
+    """In place: k_buf/v_buf [B,T_kv,C] tokens [t0, t0+T_loc) <- k_fresh/v_fresh [B,T_loc,C]."""
+    _dev(k_buf, v_buf, k_fresh, v_fresh)
+    dt = _dt(k_buf, v_buf, k_fresh, v_fresh)
+    B, T_kv, C = k_buf.shape
+    if tuple(v_buf.shape) != (B, T_kv, C) or k_fresh.shape != v_fresh.shape or \
+            k_fresh.shape[0] != B or k_fresh.shape[2] != C:
+        raise ValueError("shape mismatch")
+    check(lib().dp_kv_buffer_splice(_p(k_buf), _p(v_buf), _p(k_fresh), _p(v_fresh), B, T_kv, C,
+                                    t0, k_fresh.shape[1], dt, _stream()), "dp_kv_buffer_splice")
+
+
+def dp_attn_stale_kv_workspace(B, H, Tq, T_kv, d, dtype) -> int:
+    return lib().dp_attn_stale_kv_workspace(B, H, Tq, T_kv, d, _DT[dtype])
+
+
+def dp_attn_stale_kv(q, k_buf, v_buf, heads: int, scale: float = 0.0, out=None, ws=None):
+    """q [B,Tq,C], k_buf/v_buf [B,T_kv,C] -> out [B,Tq,C]; scale <= 0 means 1/sqrt(d)."""
+    _dev(q, k_buf, v_buf, out)
+    dt = _dt(q, k_buf, v_buf, out)
+    B, Tq, C = q.shape
+    T_kv = k_buf.shape[1]
+    if tuple(k_buf.shape) != (B, T_kv, C) or tuple(v_buf.shape) != (B, T_kv, C) or C % heads:
+        raise ValueError("shape mismatch")
+    d = C // heads
+    if out is None:
+        out = torch.empty_like(q)
+    need = lib().dp_attn_stale_kv_workspace(B, heads, Tq, T_kv, d, dt)
+    if ws is None:
+        ws = _ws(need, q.device)
+    check(lib().dp_attn_stale_kv(_p(q), _p(k_buf), _p(v_buf), _p(out), B, heads, Tq, T_kv, d,
+                                 float(scale), dt, _p(ws), 0 if ws is None else ws.numel(),
+                                 _stream()), "dp_attn_stale_kv")
+    return out
+
+
+def dp_conv3x3_stale_halo(x, halo_top, halo_bot, w, bias=None, y=None):
+    """x [B,h,W,Cin], halos [B,W,Cin] or None, w [Cout,3,3,Cin] -> y [B,h,W,Cout]."""
+    _dev(x, halo_top, halo_bot, w, y, f32=(bias,))
+    dt = _dt(x, halo_top, halo_bot, w, y)
+    B, h, W, Cin = x.shape
+    Cout = w.shape[0]
+    if tuple(w.shape) != (Cout, 3, 3, Cin):
+        raise ValueError("w must be [Cout,3,3,Cin]")
+    for hl in (halo_top, halo_bot):
+        if hl is not None and tuple(hl.shape) != (B, W, Cin):
+            raise ValueError("halo must be [B,W,Cin]")
+    if y is None:
+        y = torch.empty((B, h, W, Cout), dtype=x.dtype, device=x.device)
+    check(lib().dp_conv3x3_stale_halo(_p(x), _p(halo_top), _p(halo_bot), _p(w), _p(bias), _p(y),
+                                      B, h, W, Cin, Cout, dt, _stream()), "dp_conv3x3_stale_halo")
+    return y
+
+
+def dp_groupnorm_stale_stats_workspace(B, T_loc, C, G) -> int:
+    return lib().dp_groupnorm_stale_stats_workspace(B, T_loc, C, G)
+
+
+def dp_groupnorm_stale_stats(x, stale_sums, rank: int, T_total: int, gamma=None, beta=None,
+                             eps: float = 1e-5, fuse_silu: bool = False, G: int = 32, y=None,
+                             fresh_sums_out=None, ws=None):
+    """x [B,T_loc,C], stale_sums [N,B,G,2] f32 -> y [B,T_loc,C] (fresh sums into fresh_sums_out)."""
+    _dev(x, y, f32=(stale_sums, gamma, beta, fresh_sums_out))
+    dt = _dt(x, y)
+    B, T, C = x.shape
+    n_patches = 1 if stale_sums is None else stale_sums.shape[0]
+    if stale_sums is not None and tuple(stale_sums.shape) != (n_patches, B, G, 2):
+        raise ValueError("stale_sums must be [N,B,G,2]")
+    if y is None:
+        y = torch.empty_like(x)
+    need = lib().dp_groupnorm_stale_stats_workspace(B, T, C, G)
+    if ws is None:
+        ws = _ws(need, x.device)
+    check(lib().dp_groupnorm_stale_stats(_p(x), _p(stale_sums), n_patches, rank, T_total, _p(gamma),
+                                         _p(beta), float(eps), int(bool(fuse_silu)), _p(y),
+                                         _p(fresh_sums_out), B, T, C, G, dt, _p(ws),
+                                         0 if ws is None else ws.numel(), _stream()),
+          "dp_groupnorm_stale_stats")
+    return y
+
+
+def dp_linear(x, w, bias=None, y=None):
+    """x [..., Cin], w [Cout, Cin] -> y [..., Cout]."""
+    _dev(x, w, y, f32=(bias,))
+    dt = _dt(x, w, y)
+    Cout, Cin = w.shape
+    if x.shape[-1] != Cin:
+        raise ValueError("x last dim must equal Cin")
+    M = x.numel() // Cin
+    if y is None:
+        y = torch.empty(x.shape[:-1] + (Cout,), dtype=x.dtype, device=x.device)
+    check(lib().dp_linear(_p(x), _p(w), _p(bias), _p(y), M, Cin, Cout, dt, _stream()), "dp_linear")
+    return y

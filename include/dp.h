@@ -1,0 +1,162 @@
+/*
+ * dp.h -- C ABI of libdp, the gfx950 (MI355X) library for one rank's share of
+ * a displaced-patch (DistriFusion-style) diffusion step.
+ *
+ * The method (DistriFusion project summary, "How It Works"): the image is
+ * split across devices; after a synchronous first step every device computes
+ * its own rows fresh and takes the rest of the image from activations the
+ * other devices produced one denoising step earlier.  Each device's rows are a
+ * contiguous band of latent rows ("Benchmarking DistVAE", "Glossary":
+ * patchify).  The three displaced layer kinds are self-attention, the 3x3
+ * convolution and GroupNorm ("OTIL for SDXL on 4x L40S", "What is implemented
+ * where"); their stale state is the attention K/V buffers, the conv halo rows
+ * (same page, "Read this before interpreting the numbers", item 3) and two
+ * scalars per GroupNorm group ("What is implemented where").
+ *
+ * Conventions for every call:
+ *  - Activations are token-major, channels last: [B, T, C] with token
+ *    t = row * W + col, so a rank's row band is one contiguous token range.
+ *  - All tensor pointers are device memory owned by the caller; the library
+ *    never allocates, frees or retains them.  Tensors are dense and
+ *    contiguous in the stated layout.  Inputs and outputs must not overlap,
+ *    except that dp_kv_buffer_splice updates its buffers in place.
+ *  - `dt` is the storage type of every activation/weight tensor of a call.
+ *    Statistics, GroupNorm gamma/beta and biases are always float32.
+ *  - Calls are asynchronous: arguments are validated on the host first (a
+ *    non-OK return has enqueued nothing and written nothing), then work is
+ *    enqueued on `stream` and the call returns.  Faults during execution
+ *    surface at the caller's next synchronisation of that stream.
+ *  - The library holds no state between calls apart from a thread-local
+ *    error string.  Calls on one stream are ordered; concurrent calls on
+ *    different streams must not share output buffers or workspaces.
+ */
+#ifndef DP_H_
+#define DP_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DP_OK = 0,
+  DP_ERR_INVALID_ARG = 1, /* NULL required pointer, non-positive size, inconsistent shapes */
+  DP_ERR_UNSUPPORTED = 2, /* valid arguments with no kernel for that shape/dtype */
+  DP_ERR_HIP = 3          /* the HIP runtime reported an error at launch */
+} dp_status;
+
+typedef enum { DP_F32 = 0, DP_BF16 = 1 } dp_dtype;
+
+/* Static description of a status code (never NULL). */
+const char* dp_status_string(dp_status s);
+/* Detail of the last non-OK return on the calling thread ("" if none). */
+const char* dp_last_error(void);
+
+/*
+ * K/V buffer splice.  Stale state of a displaced self-attention layer is a
+ * full-image K/V buffer per layer ("Tensor Parallelism with Stale
+ * Activations ...", xDiT issue thread, maintainer's first reply: full spatial
+ * shape K/V for every layer).  Each step the rank's own rows are replaced by
+ * fresh values while every other row keeps its stale content; a position is
+ * either fresh or stale, never a blend ("OTIL ...", "Self-tests").
+ *
+ * k_buf, v_buf     [B, T_kv, C], updated in place.
+ * k_fresh, v_fresh [B, T_loc, C].
+ * Tokens [t0, t0 + T_loc) of each batch item are overwritten bit for bit;
+ * every other token is left untouched.  The copy is byte-exact for both dtypes.
+ * Errors: INVALID_ARG for a NULL pointer, B/T_kv/C/T_loc <= 0, t0 < 0 or
+ * t0 + T_loc > T_kv, or fresh rows overlapping the buffers.
+ */
+dp_status dp_kv_buffer_splice(void* k_buf, void* v_buf, const void* k_fresh, const void* v_fresh,
+                              int64_t B, int64_t T_kv, int64_t C, int64_t t0, int64_t T_loc,
+                              dp_dtype dt, hipStream_t stream);
+
+/*
+ * Attention of the rank's query rows over the whole spliced K/V buffer
+ * ("OTIL ...", "What is implemented where": the displaced self-attention
+ * layer; xDiT issue thread: fresh local and stale remote values mixed).
+ * For each batch b, head h, query i:
+ *   o = sum_j softmax_j(scale * <q_i, k_j>) v_j   over all T_kv keys, no mask.
+ * Head h occupies channels [h*d, (h+1)*d) of the C = H*d channels.
+ *
+ * q     [B, Tq, H*d];  k_buf, v_buf [B, T_kv, H*d];  out [B, Tq, H*d].
+ * scale <= 0 selects 1/sqrt(d).  Softmax and accumulation run in float32;
+ * in bf16 the probabilities are rounded to bf16 before the P*V product.
+ * Supported: bf16 with d = 64; f32 with d in {32, 64}.
+ * ws/ws_bytes: caller-owned device scratch of at least
+ * dp_attn_stale_kv_workspace(...) bytes (NULL allowed when that is 0).
+ * Errors: INVALID_ARG for NULL pointers, sizes <= 0 or a workspace that is too
+ * small; UNSUPPORTED for other d or dtype combinations.
+ */
+size_t dp_attn_stale_kv_workspace(int64_t B, int64_t H, int64_t Tq, int64_t T_kv, int64_t d,
+                                  dp_dtype dt);
+dp_status dp_attn_stale_kv(const void* q, const void* k_buf, const void* v_buf, void* out,
+                           int64_t B, int64_t H, int64_t Tq, int64_t T_kv, int64_t d, float scale,
+                           dp_dtype dt, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * 3x3 convolution of the rank's rows whose missing neighbour rows come from
+ * the stale halo buffers ("OTIL ...", "What is implemented where": the
+ * displaced conv; "Benchmarking DistVAE", "Glossary": a halo is the
+ * neighbouring rows a sharded convolution needs).  Stride 1, cross-correlation:
+ *   y[b,i,x,o] = bias[o] + sum_{dy,dx in -1..1} sum_c w[o,dy+1,dx+1,c] * src(b,i+dy,x+dx,c)
+ * where src row -1 is halo_top, row h is halo_bot, and columns outside
+ * [0, W) are zero.
+ *
+ * x [B, h, W, Cin]; halo_top, halo_bot [B, W, Cin] or NULL (an image edge:
+ * zeros); w [Cout, 3, 3, Cin]; bias [Cout] float32 or NULL; y [B, h, W, Cout].
+ * Supported: bf16 with Cin % 64 == 0 and Cout % 32 == 0 (MFMA path); f32 any size.
+ * Errors: INVALID_ARG for NULL x/w/y or sizes <= 0; UNSUPPORTED otherwise.
+ */
+dp_status dp_conv3x3_stale_halo(const void* x, const void* halo_top, const void* halo_bot,
+                                const void* w, const float* bias, void* y,
+                                int64_t B, int64_t h, int64_t W, int64_t Cin, int64_t Cout,
+                                dp_dtype dt, hipStream_t stream);
+
+/*
+ * GroupNorm of the rank's tokens with statistics of the whole image: fresh
+ * sums over the local tokens plus the stale sums the other patches produced
+ * one step earlier ("OTIL ...", "What is implemented where": two scalars per
+ * group decide slice brightness and contrast; "Manual runs": per-slice
+ * statistics show as a contrast step at the seam; xDiT issue thread: partial
+ * stale values).  For batch b and group g (channels [g*C/G, (g+1)*C/G)):
+ *   S = (sum x, sum x^2 over local tokens) + sum_{p != rank} stale_sums[p,b,g,:]
+ *   n = T_total * C/G;  mean = S0/n;  var = max(S1/n - mean^2, 0)
+ *   y = (x - mean) / sqrt(var + eps) * gamma[c] + beta[c]   (then y*sigmoid(y) if fuse_silu)
+ *
+ * x [B, T_loc, C]; stale_sums [n_patches, B, G, 2] float32, entry [rank] is
+ * never read; gamma, beta [C] float32 or NULL (1 and 0); y [B, T_loc, C];
+ * fresh_sums_out [B, G, 2] float32 receives the local sums, or NULL.
+ * ws/ws_bytes: at least dp_groupnorm_stale_stats_workspace(...) bytes.
+ * Supported: C % G == 0, C % 8 == 0 (bf16) or C % 4 == 0 (f32), C <= 2048.
+ * Errors: INVALID_ARG for NULL x/y/stale_sums (stale_sums may be NULL only
+ * when n_patches == 1), sizes <= 0, rank outside [0, n_patches), T_total < T_loc,
+ * eps < 0, C % G != 0, or a workspace that is too small.
+ */
+size_t dp_groupnorm_stale_stats_workspace(int64_t B, int64_t T_loc, int64_t C, int64_t G);
+dp_status dp_groupnorm_stale_stats(const void* x, const float* stale_sums, int64_t n_patches,
+                                   int64_t rank, int64_t T_total, const float* gamma,
+                                   const float* beta, float eps, int fuse_silu, void* y,
+                                   float* fresh_sums_out, int64_t B, int64_t T_loc, int64_t C,
+                                   int64_t G, dp_dtype dt, void* ws, size_t ws_bytes,
+                                   hipStream_t stream);
+
+/*
+ * Dense projection of the rank's own rows (the Q/K/V and output projections
+ * inside the displaced self-attention layer; only local rows are projected,
+ * stale rows are never recomputed):
+ *   y[m, o] = sum_c x[m, c] * w[o, c] (+ bias[o])
+ * x [M, Cin]; w [Cout, Cin]; bias [Cout] float32 or NULL; y [M, Cout].
+ * Supported: bf16 with Cin % 64 == 0 and Cout % 32 == 0; f32 any size.
+ * Errors: INVALID_ARG for NULL x/w/y or sizes <= 0; UNSUPPORTED otherwise.
+ */
+dp_status dp_linear(const void* x, const void* w, const float* bias, void* y, int64_t M,
+                    int64_t Cin, int64_t Cout, dp_dtype dt, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DP_H_ */
