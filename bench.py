@@ -1,0 +1,406 @@
+#!/usr/bin/env python3
+"""Benchmark of one rank's share of a displaced-patch diffusion step on one MI355X.
+
+One step = every hot-path op of the share, in order, through libdp:
+  single-level workloads: Q/K/V projections of the local rows -> K/V buffer
+      splice -> attention over the full-image buffer -> output projection ->
+      conv3x3 with stale halo rows -> GroupNorm with stale remote sums;
+  two-level workload: GN+SiLU -> conv -> GN+SiLU -> conv at the conv level, and
+      projections -> splice -> attention -> output projection at the
+      attention level.
+Inputs are synthetic (seeded) and resident in HBM before timing.  The stale
+state (remote K/V rows, halo rows, remote GroupNorm sums) is the previous
+step's full-image result plus N(0, 0.05^2) noise, computed on the GPU before
+timing.
+
+Prints one JSON line.  value = algorithmic dense FLOPs of the step (attention
++ projections + convs) / measured step time, in TFLOP/s.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3     # MI355X fp32 vector
+PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
+DEFAULT_WORKLOAD = "sdxl3840_l240_c640"
+METRIC = "rank-share step TFLOP/s (attn+conv) & GroupNorm GB/s; % of MI355X roofline"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ----------------------------------------------------------------- GPU state
+class Share:
+    """Device tensors of one rank's share plus its stale state."""
+
+    def __init__(self, w, torch, ops, synth):
+        self.w, self.torch, self.ops = w, torch, ops
+        self.dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+        dev = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).cuda().to(self.dt)
+        f32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).cuda()
+        noise = lambda name, shape: f32(synth.stale_noise(w, name, shape))
+        B = w.B
+        # ---------------- attention level
+        a = synth.attention_block_inputs(w)
+        H, Wd, C = w.attn_H, w.attn_W, w.attn_C
+        T = H * Wd
+        x_full = dev(a["x_full"]).view(B, T, C)
+        self.wq, self.wk, self.wv, self.wo = (dev(a[k]) for k in ("wq", "wk", "wv", "wo"))
+        k_full = torch.empty((B, T, C), dtype=self.dt, device="cuda")
+        v_full = torch.empty_like(k_full)
+        for p in range(w.N):
+            a0, a1 = w.attn_rows(p)
+            xp = x_full[:, a0 * Wd:a1 * Wd].contiguous()
+            k_full[:, a0 * Wd:a1 * Wd] = ops.dp_linear(xp, self.wk)
+            v_full[:, a0 * Wd:a1 * Wd] = ops.dp_linear(xp, self.wv)
+        # stale buffers: the previous step's full-image K/V plus noise
+        self.k_buf = (k_full.float() + f32(a["k_noise"])).to(self.dt)
+        self.v_buf = (v_full.float() + f32(a["v_noise"])).to(self.dt)
+        r0, r1 = w.attn_rows()
+        self.t0 = r0 * Wd
+        self.x_loc = x_full[:, r0 * Wd:r1 * Wd].contiguous()
+        Tq = w.Tq
+        mk = lambda *s: torch.empty(*s, dtype=self.dt, device="cuda")
+        self.q, self.kf, self.vf = mk(B, Tq, C), mk(B, Tq, C), mk(B, Tq, C)
+        self.o, self.y = mk(B, Tq, C), mk(B, Tq, C)
+        self.attn_ws = None
+        n = ops.dp_attn_stale_kv_workspace(B, w.heads, Tq, T, C // w.heads, self.dt)
+        if n:
+            self.attn_ws = torch.empty(n, dtype=torch.uint8, device="cuda")
+        # ---------------- conv / GroupNorm level
+        G = w.G
+        self.G = G
+        hc, Wc, Cc, Hc = w.conv_h, w.conv_W, w.conv_C, w.conv_H
+        c0, c1 = w.conv_rows()
+        self.hc, Tc = hc, hc * Wc
+        self.convs, self.gns = [], []
+        n_conv = 2 if w.two_level else 1
+        for i in range(n_conv):
+            cv = synth.conv_inputs(w, i)
+            self.convs.append({"w": dev(cv["w"]), "b": f32(cv["bias"]), "cv": cv})
+            gn = synth.groupnorm_inputs(w, i)
+            self.gns.append({"gamma": f32(gn["gamma"]), "beta": f32(gn["beta"])})
+        # The previous step with stale == fresh, rebuilt rank by rank with the
+        # same launch shapes as the timed step; stale state = that + noise.
+        rows_c = [w.conv_rows(p) for p in range(w.N)]
+        band = lambda full, p: full[:, rows_c[p][0] * Wc:rows_c[p][1] * Wc]
+
+        def halos(full_img, p, noise_t=None, noise_b=None):
+            r0, r1 = rows_c[p]
+            top = full_img[:, r0 - 1] if r0 > 0 else None
+            bot = full_img[:, r1] if r1 < Hc else None
+            if noise_t is not None:
+                top = None if top is None else (top.float() + noise_t).to(self.dt)
+                bot = None if bot is None else (bot.float() + noise_b).to(self.dt)
+            return (None if top is None else top.contiguous(), None if bot is None else bot.contiguous())
+
+        def sums_of(full):
+            out = torch.zeros((w.N, B, G, 2), dtype=torch.float32, device="cuda")
+            for p in range(w.N):
+                ops.dp_groupnorm_stale_stats(band(full, p).contiguous(), None, 0, Tc, None, None,
+                                             w.eps, False, G, fresh_sums_out=out[p])
+            return out
+
+        def full_gn(full, i, silu):
+            sums = sums_of(full)
+            out = torch.empty_like(full)
+            for p in range(w.N):
+                y = ops.dp_groupnorm_stale_stats(band(full, p).contiguous(), sums, p, Hc * Wc,
+                                                 self.gns[i]["gamma"], self.gns[i]["beta"], w.eps,
+                                                 silu, G)
+                band(out, p).copy_(y)
+            return out
+
+        def full_conv(full, i):
+            img = full.view(B, Hc, Wc, Cc)
+            out = torch.empty((B, Hc * Wc, Cc), dtype=self.dt, device="cuda")
+            for p in range(w.N):
+                ht, hb = halos(img, p)
+                z = ops.dp_conv3x3_stale_halo(band(full, p).contiguous().view(B, hc, Wc, Cc), ht, hb,
+                                              self.convs[i]["w"], self.convs[i]["b"])
+                band(out, p).copy_(z.view(B, Tc, Cc))
+            return out
+
+        def stale_sums(full, i):
+            return sums_of((full.float() + noise(f"gn{i}.stale_noise", tuple(full.shape))).to(self.dt))
+
+        def stale_halos(full, i):
+            cv = self.convs[i]["cv"]
+            return halos(full.view(B, Hc, Wc, Cc), w.rank, f32(cv["halo_top_noise"]),
+                         f32(cv["halo_bot_noise"]))
+
+        if w.two_level:
+            z = dev(synth.conv_level_input(w)).view(B, Hc * Wc, Cc)
+            self.conv_in_loc = band(z, w.rank).contiguous()
+            for i in range(2):
+                self.gns[i]["stale"] = stale_sums(z, i)
+                g_full = full_gn(z, i, True)
+                self.convs[i]["ht"], self.convs[i]["hb"] = stale_halos(g_full, i)
+                z = full_conv(g_full, i)
+        else:
+            y_full = torch.empty((B, T, C), dtype=self.dt, device="cuda")
+            for p in range(w.N):
+                a0, a1 = w.attn_rows(p)
+                xp = x_full[:, a0 * Wd:a1 * Wd].contiguous()
+                y_full[:, a0 * Wd:a1 * Wd] = ops.dp_linear(
+                    ops.dp_attn_stale_kv(ops.dp_linear(xp, self.wq), k_full, v_full, w.heads), self.wo)
+            self.convs[0]["ht"], self.convs[0]["hb"] = stale_halos(y_full, 0)
+            z = full_conv(y_full, 0)
+            self.gns[0]["stale"] = stale_sums(z, 0)
+        self.gn_ws = torch.empty(ops.dp_groupnorm_stale_stats_workspace(B, Tc, Cc, G),
+                                 dtype=torch.uint8, device="cuda")
+        self.zc = [mk(B, Tc, Cc) for _ in range(2)]
+        self.gc = [mk(B, Tc, Cc) for _ in range(2)]
+        self.fresh = [torch.empty((B, G, 2), dtype=torch.float32, device="cuda") for _ in range(2)]
+        if not w.two_level:
+            self.conv_in_loc = None
+        torch.cuda.synchronize()
+
+    # one step; `mark(name)` is called after each op is enqueued
+    def step(self, mark):
+        w, ops = self.w, self.ops
+        B = w.B
+        if w.two_level:
+            hc, Wc, Cc = self.hc, w.conv_W, w.conv_C
+            x = self.conv_in_loc
+            for i in range(2):
+                gi, ci = self.gns[i], self.convs[i]
+                ops.dp_groupnorm_stale_stats(x, gi["stale"], w.rank, w.conv_H * Wc, gi["gamma"],
+                                             gi["beta"], w.eps, True, self.G, y=self.gc[i],
+                                             fresh_sums_out=self.fresh[i], ws=self.gn_ws)
+                mark("groupnorm")
+                ops.dp_conv3x3_stale_halo(self.gc[i].view(B, hc, Wc, Cc), ci["ht"], ci["hb"], ci["w"],
+                                          ci["b"], y=self.zc[i].view(B, hc, Wc, Cc))
+                mark("conv")
+                x = self.zc[i]
+        ops.dp_linear(self.x_loc, self.wq, y=self.q)
+        ops.dp_linear(self.x_loc, self.wk, y=self.kf)
+        ops.dp_linear(self.x_loc, self.wv, y=self.vf)
+        mark("proj")
+        ops.dp_kv_buffer_splice(self.k_buf, self.v_buf, self.kf, self.vf, self.t0)
+        mark("splice")
+        ops.dp_attn_stale_kv(self.q, self.k_buf, self.v_buf, w.heads, out=self.o, ws=self.attn_ws)
+        mark("attn")
+        ops.dp_linear(self.o, self.wo, y=self.y)
+        mark("proj")
+        if not w.two_level:
+            c, g = self.convs[0], self.gns[0]
+            ops.dp_conv3x3_stale_halo(self.y.view(B, self.hc, w.conv_W, w.conv_C), c["ht"], c["hb"],
+                                      c["w"], c["b"], y=self.zc[0].view(B, self.hc, w.conv_W, w.conv_C))
+            mark("conv")
+            ops.dp_groupnorm_stale_stats(self.zc[0], g["stale"], w.rank, w.conv_H * w.conv_W,
+                                         g["gamma"], g["beta"], w.eps, False, self.G, y=self.gc[0],
+                                         fresh_sums_out=self.fresh[0], ws=self.gn_ws)
+            mark("groupnorm")
+
+
+# -------------------------------------------------------------- CPU baseline
+def cpu_baseline(w, synth, seconds: float):
+    """The oracle, as it stands, on a bounded sample of the same share; each
+    op's sample time is scaled up by its own sampled fraction.  The number of
+    query rows is chosen from a 4-row probe so that the attention sample takes
+    about `seconds` on this host."""
+    import oracle
+
+    oracle.build()
+    dt = w.dtype
+    R = synth.random_tensor
+    B, C, Tkv = w.B, w.attn_C, w.T_kv
+    t = {}
+    k = R(1, "cpu.k", (B, Tkv, C), dt)
+    v = R(1, "cpu.v", (B, Tkv, C), dt)
+    wl = R(0, "cpu.w", (C, C), dt, C ** -0.5)
+    probe = min(4, w.Tq)
+    t0 = time.perf_counter()
+    oracle.attention(R(1, "cpu.q0", (B, probe, C), dt), k, v, w.heads)
+    per_row = (time.perf_counter() - t0) / probe
+    rows = int(max(8, min(w.Tq, seconds / max(per_row, 1e-9))))
+    q = R(1, "cpu.q", (B, rows, C), dt)
+    t0 = time.perf_counter()
+    oracle.attention(q, k, v, w.heads)
+    t["attn"] = (time.perf_counter() - t0) * w.Tq / rows
+    t0 = time.perf_counter()
+    for _ in range(4):
+        oracle.linear(q, wl)
+    t["proj"] = (time.perf_counter() - t0) * w.Tq / rows
+    t0 = time.perf_counter()
+    oracle.kv_buffer_splice(k[:, :w.Tq], v[:, :w.Tq], q, q, 0)
+    t["splice"] = (time.perf_counter() - t0) * w.Tq / rows
+    Cc, Wc, hc = w.conv_C, w.conv_W, w.conv_h
+    n_conv = 2 if w.two_level else 1
+    xr = R(1, "cpu.xc", (B, 1, Wc, Cc), dt)
+    hr = R(2, "cpu.hc", (B, Wc, Cc), dt)
+    cw = R(0, "cpu.cw", (Cc, 3, 3, Cc), dt, (9 * Cc) ** -0.5)
+    t0 = time.perf_counter()
+    oracle.conv3x3_halo(xr, hr, hr, cw, None)
+    t["conv"] = (time.perf_counter() - t0) * hc * n_conv
+    st = np.zeros((w.N, B, w.G, 2))
+    t0 = time.perf_counter()
+    oracle.groupnorm_stale(xr.reshape(B, Wc, Cc), st, w.rank, w.N * hc * Wc, None, None, w.eps,
+                           w.two_level, w.G)
+    t["groupnorm"] = (time.perf_counter() - t0) * hc * n_conv
+    fl = w.flops()
+    total = sum(t.values())
+    return {
+        "value": sum(fl.values()) / total / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(os.environ.get("OMP_NUM_THREADS") or os.cpu_count()),
+        "kind": "oracle",
+        "sample": (f"{rows} of {w.Tq} query rows x {B} batch items against all {Tkv} keys "
+                   f"(attention, projections, splice); 1 of {hc} output rows per conv and per "
+                   f"GroupNorm; fp64 C oracle, each op's time scaled by its sampled fraction"),
+        "step_s_extrapolated": total,
+        "per_op_s_extrapolated": {k2: round(v2, 3) for k2, v2 in t.items()},
+        "cpu_model": _cpu_model(),
+    }
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor()
+
+
+# ----------------------------------------------------------- counter traffic
+def _traffic_from_profile(w):
+    """HBM bytes per attention launch from the committed rocprofv3 counter
+    summary, if it was taken on the current attention source."""
+    path = os.path.join(ROOT, "profiles", f"attn_{w.name}_counters.txt")
+    src = os.path.join(ROOT, "displaced_patch_diffusion_amd", "csrc", "attention.hip")
+    try:
+        with open(path) as f:
+            rec = None
+            for line in f:
+                if line.startswith("RESULT "):
+                    rec = json.loads(line[len("RESULT "):])
+        with open(src, "rb") as f:
+            sha = hashlib.sha256(f.read()).hexdigest()
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("attention_hip_sha256") != sha:
+        return None
+    return rec.get("traffic_bytes_per_launch")
+
+
+# ---------------------------------------------------------------------- main
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target CPU time of the oracle's attention sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one rank's share on ONE GPU; --gpus {args.gpus} "
+              f"(WORLD_SIZE={world}) is not supported: this build has no multi-GPU path.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from displaced_patch_diffusion_amd import ops, synth
+
+    if args.workload not in synth.WORKLOADS:
+        sys.exit(f"unknown workload {args.workload}; choose from {list(synth.WORKLOADS)}")
+    w = synth.WORKLOADS[args.workload]
+    torch.cuda.set_device(0)
+    log(f"bench: workload {w.name}: building inputs")
+    share = Share(w, torch, ops, synth)
+
+    names = []
+
+    def collect(name):
+        names.append(name)
+
+    share.step(collect)
+    n_marks = len(names)
+    for _ in range(args.warmup):
+        share.step(lambda n: None)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(n_marks + 1)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(K):
+        e = ev[s]
+        e[0].record()
+        idx = [0]
+
+        def mark(_name, e=e, idx=idx):
+            idx[0] += 1
+            e[idx[0]].record()
+
+        share.step(mark)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    log(f"bench: {K} steps in {wall:.4f}s")
+
+    per_op = {}
+    for s in range(K):
+        for i, name in enumerate(names):
+            per_op.setdefault(name, 0.0)
+            per_op[name] += ev[s][i].elapsed_time(ev[s][i + 1]) * 1e-3 / K
+    fl, by = w.flops(), w.bytes()
+    step_s = wall / K
+    work = sum(fl.values())
+    value = work / step_s / 1e12
+    peak_mfma = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
+    kern = {}
+    for name, t in per_op.items():
+        if name in fl:
+            a = fl[name] / t / 1e12
+            kern[name] = {"us": round(t * 1e6, 2), "TFLOP/s": round(a, 1), "frac": round(a / peak_mfma, 4)}
+        elif name in by:
+            a = by[name] / t / 1e9
+            kern[name] = {"us": round(t * 1e6, 2), "GB/s": round(a, 1), "frac": round(a / PEAK_HBM_GBPS, 4)}
+    attn_t = per_op["attn"]
+    achieved = fl["attn"] / attn_t / 1e12
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak_mfma,
+                "unit": "TFLOP/s", "frac": round(achieved / peak_mfma, 4),
+                "traffic": _traffic_from_profile(w), "kernel": "attn_bf16_d64",
+                "work_per_launch": f"{fl['attn'] / 1e9:.2f} GFLOP"}
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": K, "warmup": args.warmup, "ms_per_step": round(step_s * 1e3, 4),
+        "higher_is_better": True, "scaling": "strong", "vs_baseline": None,
+        "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.B, "attn_level": f"{w.attn_H}x{w.attn_W}",
+                   "C_attn": w.attn_C, "heads": w.heads, "head_dim": w.head_dim,
+                   "conv_level": f"{w.conv_H}x{w.conv_W}", "C_conv": w.conv_C, "n_patches": w.N,
+                   "rank": w.rank, "Tq": w.Tq, "T_kv": w.T_kv, "parallelism": "one rank's share, 1 GPU"},
+        "roofline": roofline,
+        "kernels": kern,
+        "groupnorm_GBps": kern.get("groupnorm", {}).get("GB/s"),
+        "flops_counted": {k2: v2 for k2, v2 in fl.items()},
+    }
+    if not args.no_cpu_baseline:
+        log("bench: CPU baseline (oracle on a bounded sample)")
+        out["cpu_baseline"] = cpu_baseline(w, synth, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

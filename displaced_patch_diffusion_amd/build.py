@@ -20,6 +20,10 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libdp.so")
 
 SOURCES = ["status.cpp", "splice.hip", "groupnorm.hip", "gemm.hip", "attention.hip"]
+# Per-file extra flags.  The attention kernels take finite inputs only, so NaN
+# semantics are not kept there: fmax then maps to bare v_max3_f32 without
+# per-operand canonicalisation (infinities, used for masking, keep their meaning).
+FILE_FLAGS = {"attention.hip": ["-fno-honor-nans"]}
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 CFLAGS = [
@@ -33,7 +37,7 @@ CFLAGS = [
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *CFLAGS, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *CFLAGS, *FILE_FLAGS.get(src, []), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     err = "\n".join(l for l in r.stderr.splitlines()
                     if "packed-fp32-ops' is not a recognized feature" not in l)

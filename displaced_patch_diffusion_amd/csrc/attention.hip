@@ -30,16 +30,42 @@
 // in float32 with expf: the correctness path for fp32 shares.
 #include <math.h>
 
+#include <algorithm>
+#include <cmath>
+
 #include "dp_internal.h"
 
 namespace {
 
 constexpr int kD = 64;
-constexpr int kBMq = 128;  // queries per block
-constexpr int kBNk = 64;   // keys per tile
-constexpr int kKLd = kD + 8;
-constexpr int kVLd = kBNk + 8;
+constexpr int kBMq = 128;              // queries per block (4 waves x 32)
+constexpr int kBNk = 64;               // keys per tile
+constexpr int kStages = 3;             // LDS ring depth (loads run two tiles ahead)
+constexpr int kTileBytes = kBNk * kD * 2;
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kRescale = 8.0f;       // lazy rescale: probabilities may reach 2^8
+constexpr int kXcds = 8;
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// Row swizzle of a 128-byte LDS row: 16-byte chunk c of row r lives in slot
+// c ^ swz(r).  With this swizzle the K operand reads (16 rows, one chunk) and
+// the V transpose reads (4 rows x 32 bytes per 16-lane group) are free of bank
+// conflicts.
+__device__ __forceinline__ int swz(int row) { return ((row & 2) << 1) | ((row >> 2) & 3); }
+
+struct AttnArgs {
+  const bf16_t* q;
+  const bf16_t* k;
+  const bf16_t* v;
+  bf16_t* out;
+  float* part_o;    // [S][B][Tq][C] unnormalised partial outputs (split only)
+  float* part_ml;   // [S][B][H][Tq][2] running max (base 2) and row sum (split only)
+  int B, H, Tq, Tkv;
+  float c;          // scale * log2(e)
+  int n_qblk, n_split, chunk_tiles, n_tiles, units, units_per_xcd;
+};
 
 __device__ __forceinline__ bf16x8 pack8(const f32x16& s, int base) {
   u32x4 u;
@@ -48,139 +74,213 @@ __device__ __forceinline__ bf16x8 pack8(const f32x16& s, int base) {
   return __builtin_bit_cast(bf16x8, u);
 }
 
-__global__ void __launch_bounds__(256, 2)
-attn_bf16_d64(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
-              const bf16_t* __restrict__ v, bf16_t* __restrict__ out, int Tq, int Tkv, int H,
-              float c) {
-  __shared__ __attribute__((aligned(16))) bf16_t Ks[2][kBNk * kKLd];
-  __shared__ __attribute__((aligned(16))) bf16_t Vt[2][kD * kVLd];
+__device__ __forceinline__ float swap_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float swap_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// 16 bytes per lane from global memory straight into LDS: lane l's bytes land
+// at lds_dst + 16*l (global_load_lds_dwordx4; the LDS base goes through M0).
+// Issued as inline assembly so that the compiler does not treat it as a
+// pending LDS write: completion is tracked only by the explicit vmcnt waits in
+// the key loop, and the compiler's own waits can only over-wait.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"  // m0 is written on purpose; nothing else here uses it
+__device__ __forceinline__ void dma16(const void* gsrc, const char* lds_dst) {
+  typedef __attribute__((address_space(3))) const char* lds_cptr;
+  const unsigned int m0 = __builtin_amdgcn_readfirstlane(
+      static_cast<unsigned int>(reinterpret_cast<uintptr_t>((lds_cptr)lds_dst)));
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+               :
+               : "s"(m0), "v"(gsrc)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+__global__ void __launch_bounds__(256, 2) attn_bf16_d64(AttnArgs a) {
+  __shared__ __attribute__((aligned(1024))) char lds[kStages * 2 * kTileBytes];
+
+  // Work unit: blocks are dealt to the XCDs round-robin, so XCD x receives
+  // blocks x, x+8, ...; give each XCD a contiguous run of units.  Units are
+  // ordered (batch, head, key chunk, query block), so the blocks resident on
+  // one XCD share a key chunk and read it from that XCD's L2.
+  const int u = (blockIdx.x % kXcds) * a.units_per_xcd + blockIdx.x / kXcds;
+  if (u >= a.units) return;
+  const int qb = u % a.n_qblk;
+  int rest = u / a.n_qblk;
+  const int split = rest % a.n_split;
+  rest /= a.n_split;
+  const int h = rest % a.H;
+  const int b = rest / a.H;
+  const int t_begin = split * a.chunk_tiles;
+  const int t_end = min(a.n_tiles, t_begin + a.chunk_tiles);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, g = lane >> 5;
-  const int b = blockIdx.z, h = blockIdx.y;
-  const int64_t C = static_cast<int64_t>(H) * kD;
-  const int qi = blockIdx.x * kBMq + wave * 32 + l32;
-  const bool q_ok = qi < Tq;
+  const int C = a.H * kD;
+  const int qi = qb * kBMq + wave * 32 + l32;
+  const bool q_ok = qi < a.Tq;
 
   bf16x8 qop[4];
   {
-    const bf16_t* qp = q + (static_cast<int64_t>(b) * Tq + (q_ok ? qi : 0)) * C + h * kD + 8 * g;
+    const bf16_t* qp = a.q + (static_cast<int64_t>(b) * a.Tq + (q_ok ? qi : 0)) * C + h * kD + 8 * g;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const u32x4 u = q_ok ? *reinterpret_cast<const u32x4*>(qp + 16 * s) : u32x4{0u, 0u, 0u, 0u};
-      qop[s] = __builtin_bit_cast(bf16x8, u);
+    for (int st = 0; st < 4; ++st) {
+      const u32x4 w = q_ok ? *reinterpret_cast<const u32x4*>(qp + 16 * st) : u32x4{0u, 0u, 0u, 0u};
+      qop[st] = __builtin_bit_cast(bf16x8, w);
     }
+    // Consume Q here so its loads are complete before the key loop; otherwise
+    // the compiler would keep a vmcnt(0) wait for them in every iteration,
+    // which would also drain the K/V prefetch.
+    asm volatile("" ::"v"(qop[0]), "v"(qop[1]), "v"(qop[2]), "v"(qop[3]));
   }
-  // K row permutation: swap bits 2 and 3 of the row index.
+
+  // K operand: lane row l32 holds key 32*blk + pi(l32), pi = swap of row bits 2
+  // and 3; then the probabilities a lane holds per 16-key step are 8
+  // consecutive keys, the B operand layout of the P.V product.
   const int krow = (l32 & ~12) | ((l32 & 4) << 1) | ((l32 & 8) >> 1);
-
-  const bf16_t* kbase = k + static_cast<int64_t>(b) * Tkv * C + h * kD;
-  const bf16_t* vbase = v + static_cast<int64_t>(b) * Tkv * C + h * kD;
-  const int ld_key = tid >> 3, ld_ch = (tid & 7) * 8;
-  u32x4 rk[2], rv[2];
-  auto load = [&](int kt) {
-    const int key0 = kt * kBNk;
+  int koff[4];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int kk = key0 + ld_key + 32 * u;
-      rk[u] = kk < Tkv ? *reinterpret_cast<const u32x4*>(kbase + kk * C + ld_ch) : u32x4{0u, 0u, 0u, 0u};
-      const int vk = key0 + 2 * ld_key + u;
-      rv[u] = vk < Tkv ? *reinterpret_cast<const u32x4*>(vbase + vk * C + ld_ch) : u32x4{0u, 0u, 0u, 0u};
+  for (int st = 0; st < 4; ++st) koff[st] = krow * 128 + (((2 * st + g) ^ swz(krow)) << 4);
+  // V^T operand via ds_read_b64_tr_b16: in each 16-lane group, lane j = 4a+b
+  // receives element b of the 8-byte pieces addressed by lanes a, a+4, a+8,
+  // a+12.  Lane i of group (g, half) addresses key row 8g + 4h + i/4 and
+  // channel 32*db + 16*half + 4*(i%4), so lane l ends up with channel l%32 of
+  // four consecutive keys.
+  int voff[2][2];
+  {
+    const int i = lane & 15, half = (lane >> 4) & 1;
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int row = 8 * g + 4 * hh + (i >> 2);
+        const int chunk = 4 * db + 2 * half + ((i & 3) >> 1);
+        voff[db][hh] = row * 128 + ((chunk ^ swz(row)) << 4) + (i & 1) * 8;
+      }
+  }
+  // DMA assignment: wave w fills rows 16w .. 16w+15 of the K and V tiles, one
+  // 1 KB (8-row) slab per instruction; lane l writes slot l%8 of row l/8.
+  int goff[2], lrow[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int row = (2 * wave + j) * 8 + (lane >> 3);
+    lrow[j] = row;
+    goff[j] = row * C + (((lane & 7) ^ swz(row)) << 3);
+  }
+  const bf16_t* kbh = a.k + static_cast<int64_t>(b) * a.Tkv * C + h * kD;
+  const bf16_t* vbh = a.v + static_cast<int64_t>(b) * a.Tkv * C + h * kD;
+
+  auto issue = [&](int t) {
+    char* kst = lds + (t % kStages) * (2 * kTileBytes);
+    const int key0 = t * kBNk;
+    const bool ragged = key0 + kBNk > a.Tkv;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      int off = goff[j];
+      if (ragged) {  // clamp rows past the end onto the last key (masked later)
+        const int key = min(key0 + lrow[j], a.Tkv - 1);
+        off = (key - key0) * C + (goff[j] - lrow[j] * C);
+      }
+      const bf16_t* gk = kbh + static_cast<int64_t>(key0) * C + off;
+      const bf16_t* gv = vbh + static_cast<int64_t>(key0) * C + off;
+      dma16(gk, kst + (2 * wave + j) * 1024);
+      dma16(gv, kst + kTileBytes + (2 * wave + j) * 1024);
     }
   };
-  auto store = [&](int buf) {
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-      *reinterpret_cast<u32x4*>(&Ks[buf][(ld_key + 32 * u) * kKLd + ld_ch]) = rk[u];
-    // rv[0] = V[2p][d0..d0+7], rv[1] = V[2p+1][d0..d0+7]: write (V[2p][d], V[2p+1][d]) pairs.
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const unsigned int lo = (rv[0][j] & 0xFFFFu) | (rv[1][j] << 16);
-      const unsigned int hi = (rv[0][j] >> 16) | (rv[1][j] & 0xFFFF0000u);
-      *reinterpret_cast<unsigned int*>(&Vt[buf][(ld_ch + 2 * j) * kVLd + 2 * ld_key]) = lo;
-      *reinterpret_cast<unsigned int*>(&Vt[buf][(ld_ch + 2 * j + 1) * kVLd + 2 * ld_key]) = hi;
-    }
-  };
 
-  float m_run = -INFINITY, l_run = 0.f;
+  float m_ref = -INFINITY, l_part = 0.f;
   f32x16 o[2];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) o[0][i] = o[1][i] = 0.f;
+  for (int e = 0; e < 16; ++e) o[0][e] = o[1][e] = 0.f;
+  const f32x16 zero = {};
 
-  const int nt = (Tkv + kBNk - 1) / kBNk;
-  load(0);
-  store(0);
-  __syncthreads();
-  for (int kt = 0; kt < nt; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nt) load(kt + 1);
+  issue(t_begin);
+  if (t_begin + 1 < t_end) issue(t_begin + 1);
+  for (int t = t_begin; t < t_end; ++t) {
+    if (t + 1 < t_end) {
+      asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+    } else {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+    __syncthreads();  // tile t visible to all waves; stage (t+2)%3 no longer read
+    if (t + 2 < t_end) issue(t + 2);
 
-    f32x16 s[2];
+    const char* ks = lds + (t % kStages) * (2 * kTileBytes);
+    const char* vs = ks + kTileBytes;
+    f32x16 sc[2];
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) s[blk][i] = 0.f;
-#pragma unroll
       for (int st = 0; st < 4; ++st) {
-        const bf16x8 ka =
-            *reinterpret_cast<const bf16x8*>(&Ks[cur][(32 * blk + krow) * kKLd + 16 * st + 8 * g]);
-        s[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qop[st], s[blk], 0, 0, 0);
+        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(ks + blk * 4096 + koff[st]);
+        sc[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qop[st], st == 0 ? zero : sc[blk], 0, 0, 0);
       }
     }
-    if ((kt + 1) * kBNk > Tkv) {  // ragged last tile: mask keys beyond T_kv
+    if ((t + 1) * kBNk > a.Tkv) {  // ragged last tile
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int r = 8 * (i >> 2) + 4 * g + (i & 3);
+        for (int e = 0; e < 16; ++e) {
+          const int r = 8 * (e >> 2) + 4 * g + (e & 3);
           const int pr = (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
-          if (kt * kBNk + 32 * blk + pr >= Tkv) s[blk][i] = -INFINITY;
+          if (t * kBNk + 32 * blk + pr >= a.Tkv) sc[blk][e] = -INFINITY;
         }
     }
-    float mx = s[0][0];
+    float mx = fmaxf(sc[0][0], sc[1][0]);
 #pragma unroll
-    for (int blk = 0; blk < 2; ++blk)
+    for (int e = 1; e < 16; ++e) mx = fmaxf(mx, fmaxf(sc[0][e], sc[1][e]));
+    const float mt = swap_max(mx) * a.c;
+    if (__builtin_amdgcn_ballot_w64(mt > m_ref + kRescale)) {
+      const float m_new = fmaxf(m_ref, mt);
+      const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
+      l_part *= alpha;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[blk][i]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx * c);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    float rs = 0.f;
-#pragma unroll
-    for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(s[blk][i], c, -m_new));
-        s[blk][i] = p;
-        rs += p;
+      for (int e = 0; e < 16; ++e) {
+        o[0][e] *= alpha;
+        o[1][e] *= alpha;
       }
-    l_run = fmaf(l_run, alpha, rs);
-    m_run = m_new;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      o[0][i] *= alpha;
-      o[1][i] *= alpha;
+      m_ref = m_new;
     }
+    bf16x8 pb[2][2];
+    float ls0 = 0.f, ls1 = 0.f;
 #pragma unroll
-    for (int blk = 0; blk < 2; ++blk)
+    for (int blk = 0; blk < 2; ++blk) {
 #pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        const bf16x8 pb = pack8(s[blk], 8 * s2);
-#pragma unroll
-        for (int db = 0; db < 2; ++db) {
-          const bf16x8 va = *reinterpret_cast<const bf16x8*>(
-              &Vt[cur][(32 * db + l32) * kVLd + 32 * blk + 16 * s2 + 8 * g]);
-          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, o[db], 0, 0, 0);
-        }
+      for (int e = 0; e < 16; e += 2) {
+        sc[blk][e] = __builtin_amdgcn_exp2f(fmaf(sc[blk][e], a.c, -m_ref));
+        sc[blk][e + 1] = __builtin_amdgcn_exp2f(fmaf(sc[blk][e + 1], a.c, -m_ref));
+        ls0 += sc[blk][e];
+        ls1 += sc[blk][e + 1];
       }
-    if (kt + 1 < nt) store(cur ^ 1);
-    __syncthreads();
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) pb[blk][s2] = pack8(sc[blk], 8 * s2);
+    }
+    l_part += ls0 + ls1;
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+          const char* vb = vs + blk * 4096 + s2 * 2048;
+          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vb + voff[db][0]));
+          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vb + voff[db][1]));
+          const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[blk][s2], o[db], 0, 0, 0);
+        }
   }
 
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
-  const float inv = 1.0f / l_tot;
-  if (q_ok) {
-    bf16_t* op = out + (static_cast<int64_t>(b) * Tq + qi) * C + h * kD;
+  const float l_tot = swap_sum(l_part);
+  if (!q_ok) return;
+  if (a.n_split == 1) {
+    const float inv = 1.0f / l_tot;
+    bf16_t* op = a.out + (static_cast<int64_t>(b) * a.Tq + qi) * C + h * kD;
 #pragma unroll
     for (int db = 0; db < 2; ++db)
 #pragma unroll
@@ -190,7 +290,139 @@ attn_bf16_d64(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
                     pack_bf16x2(o[db][4 * qq + 2] * inv, o[db][4 * qq + 3] * inv)};
         *reinterpret_cast<u32x2*>(op + d) = pk;
       }
+  } else {
+    float* op = a.part_o + ((static_cast<int64_t>(split) * a.B + b) * a.Tq + qi) * C + h * kD;
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq) {
+        const int d = 32 * db + 8 * qq + 4 * g;
+        *reinterpret_cast<f32x4*>(op + d) =
+            f32x4{o[db][4 * qq], o[db][4 * qq + 1], o[db][4 * qq + 2], o[db][4 * qq + 3]};
+      }
+    if (g == 0) {
+      float* ml = a.part_ml + (((static_cast<int64_t>(split) * a.B + b) * a.H + h) * a.Tq + qi) * 2;
+      ml[0] = m_ref;
+      ml[1] = l_tot;
+    }
   }
+}
+
+// Merges the key-chunk partials: o = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s.
+// One thread per (batch, query, head, 8-channel group).
+__global__ void __launch_bounds__(256)
+attn_combine(const float* __restrict__ part_o, const float* __restrict__ part_ml,
+             bf16_t* __restrict__ out, int B, int H, int Tq, int S) {
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int64_t total = static_cast<int64_t>(B) * Tq * H * 8;
+  if (idx >= total) return;
+  const int ch = static_cast<int>(idx & 7);
+  int64_t r = idx >> 3;
+  const int h = static_cast<int>(r % H);
+  r /= H;
+  const int q = static_cast<int>(r % Tq);
+  const int b = static_cast<int>(r / Tq);
+  const int C = H * kD;
+  float M = -INFINITY;
+  for (int s = 0; s < S; ++s)
+    M = fmaxf(M, part_ml[(((static_cast<int64_t>(s) * B + b) * H + h) * Tq + q) * 2]);
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float L = 0.f;
+  for (int s = 0; s < S; ++s) {
+    const float* ml = part_ml + (((static_cast<int64_t>(s) * B + b) * H + h) * Tq + q) * 2;
+    const float w = __builtin_amdgcn_exp2f(ml[0] - M);
+    L = fmaf(w, ml[1], L);
+    const float* po = part_o + ((static_cast<int64_t>(s) * B + b) * Tq + q) * C + h * kD + ch * 8;
+    const f32x4 x0 = *reinterpret_cast<const f32x4*>(po);
+    const f32x4 x1 = *reinterpret_cast<const f32x4*>(po + 4);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      acc[j] = fmaf(w, x0[j], acc[j]);
+      acc[4 + j] = fmaf(w, x1[j], acc[4 + j]);
+    }
+  }
+  const float inv = 1.0f / L;
+  u32x4 pk;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) pk[j] = pack_bf16x2(acc[2 * j] * inv, acc[2 * j + 1] * inv);
+  *reinterpret_cast<u32x4*>(out + (static_cast<int64_t>(b) * Tq + q) * C + h * kD + ch * 8) = pk;
+}
+
+struct AttnPlan {
+  int n_qblk, n_tiles, n_split, chunk_tiles, units, units_per_xcd, grid;
+  size_t ws_bytes;
+};
+
+int device_cus() {
+  static thread_local int cached_dev = -1, cached_cus = 256;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return 256;
+  }
+  if (dev != cached_dev) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && cus > 0)
+      cached_cus = cus;
+    else
+      (void)hipGetLastError();
+    cached_dev = dev;
+  }
+  return cached_cus;
+}
+
+// Resident attention blocks per CU (registers and LDS), asked of the runtime.
+int blocks_per_cu() {
+  static thread_local int cached = 0;
+  if (cached == 0) {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_bf16_d64, 256, 0) != hipSuccess || n <= 0) {
+      (void)hipGetLastError();
+      n = 2;
+    }
+    cached = n;
+  }
+  return cached;
+}
+
+// Picks the number of key chunks: each block runs one (batch, head, chunk,
+// query block) unit and the XCDs receive equal contiguous runs of units; the
+// estimated time is (rounds of resident blocks per XCD) x (tiles per unit),
+// plus the cost of the extra partial-output traffic when the keys are split.
+AttnPlan plan_attention(int64_t B, int64_t H, int64_t Tq, int64_t Tkv) {
+  AttnPlan p{};
+  p.n_qblk = static_cast<int>((Tq + kBMq - 1) / kBMq);
+  p.n_tiles = static_cast<int>((Tkv + kBNk - 1) / kBNk);
+  const int slots_per_xcd = std::max(1, device_cus() / kXcds) * blocks_per_cu();
+  const double base_units = static_cast<double>(B) * H * p.n_qblk;
+  // cost unit: one 64-key tile of one block (~1 us); the split's partial
+  // outputs cost their bytes at ~5 TB/s, i.e. ~5 MB per unit
+  const double tile_cost = 1.0;
+  const double bytes_per_tile_cost = 5.0e6;
+  double best = 1e300;
+  for (int S = 1; S <= 16 && S <= p.n_tiles; ++S) {
+    const int chunk = (p.n_tiles + S - 1) / S;
+    const int s_eff = (p.n_tiles + chunk - 1) / chunk;
+    if (s_eff != S && S > 1) continue;
+    const double units = base_units * s_eff;
+    const double per_xcd = std::ceil(units / kXcds);
+    const double rounds = std::ceil(per_xcd / slots_per_xcd);
+    double cost = rounds * chunk * tile_cost;
+    if (s_eff > 1)
+      cost += (static_cast<double>(s_eff) * 8.0 + 2.0) * B * Tq * H * kD / bytes_per_tile_cost;
+    if (cost < best * 0.999) {
+      best = cost;
+      p.n_split = s_eff;
+      p.chunk_tiles = chunk;
+    }
+  }
+  p.units = static_cast<int>(base_units) * p.n_split;
+  p.units_per_xcd = (p.units + kXcds - 1) / kXcds;
+  p.grid = p.units_per_xcd * kXcds;
+  p.ws_bytes = p.n_split > 1 ? static_cast<size_t>(p.n_split) * B * Tq * H * kD * sizeof(float) +
+                                   static_cast<size_t>(p.n_split) * B * H * Tq * 2 * sizeof(float)
+                             : 0;
+  return p;
 }
 
 // ------------------------------------------------------------------ f32 path
@@ -260,8 +492,8 @@ attn_f32(const float* __restrict__ q, const float* __restrict__ k, const float* 
 
 DP_API size_t dp_attn_stale_kv_workspace(int64_t B, int64_t H, int64_t Tq, int64_t T_kv, int64_t d,
                                          dp_dtype dt) {
-  (void)B, (void)H, (void)Tq, (void)T_kv, (void)d, (void)dt;
-  return 0;
+  if (dt != DP_BF16 || d != kD || B <= 0 || H <= 0 || Tq <= 0 || T_kv <= 0) return 0;
+  return plan_attention(B, H, Tq, T_kv).ws_bytes;
 }
 
 DP_API dp_status dp_attn_stale_kv(const void* q, const void* k_buf, const void* v_buf, void* out,
@@ -269,7 +501,6 @@ DP_API dp_status dp_attn_stale_kv(const void* q, const void* k_buf, const void* 
                                   float scale, dp_dtype dt, void* ws, size_t ws_bytes,
                                   hipStream_t stream) {
   using dp::fail;
-  (void)ws, (void)ws_bytes;
   if (!q || !k_buf || !v_buf || !out) return fail(DP_ERR_INVALID_ARG, "dp_attn_stale_kv: NULL pointer");
   if (B <= 0 || H <= 0 || Tq <= 0 || T_kv <= 0 || d <= 0)
     return fail(DP_ERR_INVALID_ARG, "dp_attn_stale_kv: sizes must be positive");
@@ -286,11 +517,35 @@ DP_API dp_status dp_attn_stale_kv(const void* q, const void* k_buf, const void* 
   const float sc = scale > 0.f ? scale : static_cast<float>(1.0 / sqrt(static_cast<double>(d)));
   dp::clear_error();
   if (dt == DP_BF16) {
-    const dim3 grid(static_cast<unsigned>((Tq + kBMq - 1) / kBMq), static_cast<unsigned>(H),
-                    static_cast<unsigned>(B));
-    hipLaunchKernelGGL(attn_bf16_d64, grid, dim3(256), 0, stream, static_cast<const bf16_t*>(q),
-                       static_cast<const bf16_t*>(k_buf), static_cast<const bf16_t*>(v_buf),
-                       static_cast<bf16_t*>(out), (int)Tq, (int)T_kv, (int)H, sc * kLog2e);
+    if (T_kv * H * d > 0x7FFFFFFF || Tq * H * d > 0x7FFFFFFF)
+      return fail(DP_ERR_UNSUPPORTED, "dp_attn_stale_kv: one batch item exceeds 2^31 elements");
+    const AttnPlan p = plan_attention(B, H, Tq, T_kv);
+    if (p.ws_bytes > 0 && (!ws || ws_bytes < p.ws_bytes))
+      return fail(DP_ERR_INVALID_ARG, "dp_attn_stale_kv: workspace %zu < %zu bytes", ws_bytes, p.ws_bytes);
+    AttnArgs args;
+    args.q = static_cast<const bf16_t*>(q);
+    args.k = static_cast<const bf16_t*>(k_buf);
+    args.v = static_cast<const bf16_t*>(v_buf);
+    args.out = static_cast<bf16_t*>(out);
+    args.part_o = static_cast<float*>(ws);
+    args.part_ml = p.ws_bytes ? args.part_o + static_cast<size_t>(p.n_split) * B * Tq * H * kD : nullptr;
+    args.B = (int)B;
+    args.H = (int)H;
+    args.Tq = (int)Tq;
+    args.Tkv = (int)T_kv;
+    args.c = sc * kLog2e;
+    args.n_qblk = p.n_qblk;
+    args.n_split = p.n_split;
+    args.chunk_tiles = p.chunk_tiles;
+    args.n_tiles = p.n_tiles;
+    args.units = p.units;
+    args.units_per_xcd = p.units_per_xcd;
+    hipLaunchKernelGGL(attn_bf16_d64, dim3(static_cast<unsigned>(p.grid)), dim3(256), 0, stream, args);
+    if (p.n_split > 1) {
+      const int64_t threads = B * Tq * H * 8;
+      hipLaunchKernelGGL(attn_combine, dim3(static_cast<unsigned>((threads + 255) / 256)), dim3(256), 0,
+                         stream, args.part_o, args.part_ml, args.out, (int)B, (int)H, (int)Tq, p.n_split);
+    }
   } else {
     const dim3 grid(static_cast<unsigned>((Tq + kFQ - 1) / kFQ), static_cast<unsigned>(H),
                     static_cast<unsigned>(B));

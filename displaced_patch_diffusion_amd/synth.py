@@ -32,10 +32,21 @@ SEED_AFFINE = 3
 # ---------------------------------------------------------------- bf16 storage
 def round_to_bf16(a: np.ndarray) -> np.ndarray:
     """Round float32 values to the nearest bfloat16 (ties to even); float32 out."""
-    a = np.ascontiguousarray(a, dtype=np.float32)
-    u = a.view(np.uint32).astype(np.uint64)
-    u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
-    return u.astype(np.uint32).view(np.float32).reshape(a.shape)
+    a = np.array(a, dtype=np.float32, order="C", copy=True)
+    if not np.isfinite(a).all():
+        raise ValueError("round_to_bf16 expects finite values")
+    u = a.reshape(-1).view(np.uint32)
+    bias = np.empty(max(1, min(u.size, 1 << 20)), dtype=np.uint32)
+    # finite floats are <= 0xFF7FFFFF, so adding at most 0x8000 cannot wrap
+    for i in range(0, u.size, bias.size):
+        seg = u[i:i + bias.size]
+        b = bias[:seg.size]
+        np.right_shift(seg, 16, out=b)
+        b &= 1
+        b += 0x7FFF
+        seg += b
+        seg &= 0xFFFF0000
+    return a
 
 
 def bf16_bits(a: np.ndarray) -> np.ndarray:
@@ -145,7 +156,7 @@ class Workload:
         n_gn = 2 if self.two_level else 1
         gn = n_gn * 2 * self.B * self.conv_T * self.conv_C * e
         splice = 4 * self.B * self.Tq * self.attn_C * e
-        return {"gn": gn, "splice": splice}
+        return {"groupnorm": gn, "splice": splice}
 
 
 def _single(name, dtype, H, W, C, heads, d, B, N, rank, note) -> Workload:

@@ -316,4 +316,7 @@ def test_stale_equals_fresh_ranks_concat_on_gpu():
         ops.dp_kv_buffer_splice(kb, vb, ops.dp_linear(xl, wk), ops.dp_linear(xl, wv), r0 * Wd)
         parts.append(ops.dp_attn_stale_kv(ops.dp_linear(xl, wq), kb, vb, w.heads))
     cat = torch.cat(parts, 1)
-    assert torch.equal(cat, ref)  # identical kernels on identical inputs: bitwise equal
+    # The key-chunk split chosen for the full image (4096 queries) differs from
+    # the one for a share (1024 queries), so the summation order differs: the
+    # property holds to the bf16 tolerance, not bit for bit.
+    assert_close(host(cat), host(ref), "bf16", "stale==fresh concatenation")
