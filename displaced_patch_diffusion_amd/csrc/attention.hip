@@ -91,19 +91,29 @@ __device__ __forceinline__ float swap_sum(float x) {
 // the key loop, and the compiler's own waits can only over-wait.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"  // m0 is written on purpose; nothing else here uses it
-__device__ __forceinline__ void dma16(const void* gsrc, const char* lds_dst) {
-  typedef __attribute__((address_space(3))) const char* lds_cptr;
-  const unsigned int m0 = __builtin_amdgcn_readfirstlane(
-      static_cast<unsigned int>(reinterpret_cast<uintptr_t>((lds_cptr)lds_dst)));
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+// 16 bytes per lane from a buffer straight into LDS: lane l's bytes land at
+// M0 + 16*l (buffer_load_dwordx4 ... lds).  Reads at offsets at or beyond the
+// descriptor's num_records return zeros.  Issued as inline assembly so that
+// the compiler does not treat it as a pending LDS write: completion is
+// tracked only by the explicit vmcnt waits in the key loop, and the compiler's
+// own waits can only over-wait.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rsrc, int voff, unsigned int m0) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                :
-               : "s"(m0), "v"(gsrc)
+               : "s"(m0), "v"(voff), "s"(rsrc)
                : "memory", "m0");
 }
 #pragma clang diagnostic pop
 
+template <int S>
+struct Stage {
+  static constexpr int value = S;
+};
+
 __global__ void __launch_bounds__(256, 2) attn_bf16_d64(AttnArgs a) {
+  // K tiles at stage*8 KB, V tiles at 24 KB + stage*8 KB.
   __shared__ __attribute__((aligned(1024))) char lds[kStages * 2 * kTileBytes];
+  constexpr int kVring = kStages * kTileBytes;
 
   // Work unit: blocks are dealt to the XCDs round-robin, so XCD x receives
   // blocks x, x+8, ...; give each XCD a contiguous run of units.  Units are
@@ -126,13 +136,18 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_d64(AttnArgs a) {
   const int qi = qb * kBMq + wave * 32 + l32;
   const bool q_ok = qi < a.Tq;
 
+  // Q, pre-multiplied by scale*log2(e) in float32 and rounded once to bf16,
+  // so that an accumulator started at -m_ref holds the exponent directly.
   bf16x8 qop[4];
   {
     const bf16_t* qp = a.q + (static_cast<int64_t>(b) * a.Tq + (q_ok ? qi : 0)) * C + h * kD + 8 * g;
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
       const u32x4 w = q_ok ? *reinterpret_cast<const u32x4*>(qp + 16 * st) : u32x4{0u, 0u, 0u, 0u};
-      qop[st] = __builtin_bit_cast(bf16x8, w);
+      u32x4 sw;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) sw[j] = pack_bf16x2(bf16_lo(w[j]) * a.c, bf16_hi(w[j]) * a.c);
+      qop[st] = __builtin_bit_cast(bf16x8, sw);
     }
     // Consume Q here so its loads are complete before the key loop; otherwise
     // the compiler would keep a vmcnt(0) wait for them in every iteration,
@@ -161,67 +176,63 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_d64(AttnArgs a) {
       for (int hh = 0; hh < 2; ++hh) {
         const int row = 8 * g + 4 * hh + (i >> 2);
         const int chunk = 4 * db + 2 * half + ((i & 3) >> 1);
-        voff[db][hh] = row * 128 + ((chunk ^ swz(row)) << 4) + (i & 1) * 8;
+        voff[db][hh] = kVring + row * 128 + ((chunk ^ swz(row)) << 4) + (i & 1) * 8;
       }
   }
-  // DMA assignment: wave w fills rows 16w .. 16w+15 of the K and V tiles, one
-  // 1 KB (8-row) slab per instruction; lane l writes slot l%8 of row l/8.
-  int goff[2], lrow[2];
+  // DMA: wave w fills rows 16w .. 16w+15 of each tile, one 1 KB (8-row) slab
+  // per instruction; lane l writes slot l%8 of row l/8, i.e. chunk
+  // (l%8) ^ swz(row) of that row.
+  int gbyte[2];
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int row = (2 * wave + j) * 8 + (lane >> 3);
-    lrow[j] = row;
-    goff[j] = row * C + (((lane & 7) ^ swz(row)) << 3);
+    gbyte[j] = (row * C + (((lane & 7) ^ swz(row)) << 3)) * 2;
   }
+  const unsigned int lds0 = __builtin_amdgcn_readfirstlane(
+      static_cast<unsigned int>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)lds)) +
+      wave * 2048);
   const bf16_t* kbh = a.k + static_cast<int64_t>(b) * a.Tkv * C + h * kD;
   const bf16_t* vbh = a.v + static_cast<int64_t>(b) * a.Tkv * C + h * kD;
+  // Bytes from a (batch, head) base to the end of that batch item's buffer.
+  const int64_t span = (static_cast<int64_t>(a.Tkv) * C - h * kD) * 2;
 
-  auto issue = [&](int t) {
-    char* kst = lds + (t % kStages) * (2 * kTileBytes);
-    const int key0 = t * kBNk;
-    const bool ragged = key0 + kBNk > a.Tkv;
+  auto issue = [&](int t, int stage) {
+    const int64_t off = static_cast<int64_t>(t) * kBNk * C;  // elements
+    const int nrec = static_cast<int>(span - off * 2);       // rows past T_kv read as 0
+    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)(kbh + off), 0, nrec, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)(vbh + off), 0, nrec, 0x00020000);
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      int off = goff[j];
-      if (ragged) {  // clamp rows past the end onto the last key (masked later)
-        const int key = min(key0 + lrow[j], a.Tkv - 1);
-        off = (key - key0) * C + (goff[j] - lrow[j] * C);
-      }
-      const bf16_t* gk = kbh + static_cast<int64_t>(key0) * C + off;
-      const bf16_t* gv = vbh + static_cast<int64_t>(key0) * C + off;
-      dma16(gk, kst + (2 * wave + j) * 1024);
-      dma16(gv, kst + kTileBytes + (2 * wave + j) * 1024);
+      dma16(rk, gbyte[j], lds0 + stage * kTileBytes + j * 1024);
+      dma16(rv, gbyte[j], lds0 + kVring + stage * kTileBytes + j * 1024);
     }
   };
 
-  float m_ref = -INFINITY, l_part = 0.f;
-  f32x16 o[2];
+  float m_ref = 0.f, l_part = 0.f;  // m_ref: base-2 reference the scores are shifted by
+  f32x16 o[2], bias;
 #pragma unroll
-  for (int e = 0; e < 16; ++e) o[0][e] = o[1][e] = 0.f;
-  const f32x16 zero = {};
+  for (int e = 0; e < 16; ++e) o[0][e] = o[1][e] = bias[e] = 0.f;
 
-  issue(t_begin);
-  if (t_begin + 1 < t_end) issue(t_begin + 1);
-  for (int t = t_begin; t < t_end; ++t) {
+  // One tile: scores, softmax and P.V from LDS stage S; tile t+2 is issued
+  // into stage (S+2)%3 first.
+  auto step = [&](auto stage_c, int t) {
+    constexpr int S = decltype(stage_c)::value;
     if (t + 1 < t_end) {
-      asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+      asm volatile("s_waitcnt vmcnt(4)" ::: "memory");  // tile t done, t+1 may be in flight
     } else {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
-    __syncthreads();  // tile t visible to all waves; stage (t+2)%3 no longer read
-    if (t + 2 < t_end) issue(t + 2);
+    __syncthreads();  // tile t visible; stage of tile t-1 no longer read
+    if (t + 2 < t_end) issue(t + 2, (S + 2) % 3);
 
-    const char* ks = lds + (t % kStages) * (2 * kTileBytes);
-    const char* vs = ks + kTileBytes;
     f32x16 sc[2];
 #pragma unroll
-    for (int blk = 0; blk < 2; ++blk) {
+    for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
       for (int st = 0; st < 4; ++st) {
-        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(ks + blk * 4096 + koff[st]);
-        sc[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qop[st], st == 0 ? zero : sc[blk], 0, 0, 0);
+        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(lds + S * kTileBytes + blk * 4096 + koff[st]);
+        sc[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qop[st], st == 0 ? bias : sc[blk], 0, 0, 0);
       }
-    }
     if ((t + 1) * kBNk > a.Tkv) {  // ragged last tile
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk)
@@ -235,31 +246,44 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_d64(AttnArgs a) {
     float mx = fmaxf(sc[0][0], sc[1][0]);
 #pragma unroll
     for (int e = 1; e < 16; ++e) mx = fmaxf(mx, fmaxf(sc[0][e], sc[1][e]));
-    const float mt = swap_max(mx) * a.c;
-    if (__builtin_amdgcn_ballot_w64(mt > m_ref + kRescale)) {
-      const float m_new = fmaxf(m_ref, mt);
-      const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
-      l_part *= alpha;
+    const float mt = swap_max(mx);  // tile max relative to m_ref
+    if (t == t_begin || __builtin_amdgcn_ballot_w64(mt > kRescale)) {
+      // Move the reference: on the first tile to the tile max (o and l are
+      // still zero), later only when a score would exceed 2^kRescale.
+      const float delta = t == t_begin ? mt : fmaxf(mt, 0.f);
+      if (t != t_begin) {
+        const float alpha = __builtin_amdgcn_exp2f(-delta);
+        l_part *= alpha;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          o[0][e] *= alpha;
+          o[1][e] *= alpha;
+        }
+      }
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        o[0][e] *= alpha;
-        o[1][e] *= alpha;
+        sc[0][e] -= delta;
+        sc[1][e] -= delta;
       }
-      m_ref = m_new;
+      m_ref += delta;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) bias[e] = -m_ref;
     }
     bf16x8 pb[2][2];
     float ls0 = 0.f, ls1 = 0.f;
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
 #pragma unroll
-      for (int e = 0; e < 16; e += 2) {
-        sc[blk][e] = __builtin_amdgcn_exp2f(fmaf(sc[blk][e], a.c, -m_ref));
-        sc[blk][e + 1] = __builtin_amdgcn_exp2f(fmaf(sc[blk][e + 1], a.c, -m_ref));
-        ls0 += sc[blk][e];
-        ls1 += sc[blk][e + 1];
-      }
+      for (int e = 0; e < 16; ++e) sc[blk][e] = __builtin_amdgcn_exp2f(sc[blk][e]);
 #pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) pb[blk][s2] = pack8(sc[blk], 8 * s2);
+      for (int s2 = 0; s2 < 2; ++s2) {
+        pb[blk][s2] = pack8(sc[blk], 8 * s2);
+#pragma unroll
+        for (int j = 0; j < 8; j += 2) {
+          ls0 += sc[blk][8 * s2 + j];
+          ls1 += sc[blk][8 * s2 + j + 1];
+        }
+      }
     }
     l_part += ls0 + ls1;
 #pragma unroll
@@ -268,12 +292,20 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_d64(AttnArgs a) {
       for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
-          const char* vb = vs + blk * 4096 + s2 * 2048;
+          const char* vb = lds + S * kTileBytes + blk * 4096 + s2 * 2048;
           const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vb + voff[db][0]));
           const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vb + voff[db][1]));
           const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
           o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[blk][s2], o[db], 0, 0, 0);
         }
+  };
+
+  issue(t_begin, 0);
+  if (t_begin + 1 < t_end) issue(t_begin + 1, 1);
+  for (int t = t_begin; t < t_end; t += 3) {
+    step(Stage<0>{}, t);
+    if (t + 1 < t_end) step(Stage<1>{}, t + 1);
+    if (t + 2 < t_end) step(Stage<2>{}, t + 2);
   }
 
   const float l_tot = swap_sum(l_part);
