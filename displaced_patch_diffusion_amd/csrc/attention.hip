@@ -105,6 +105,18 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rsrc, int voff, uns
 }
 #pragma clang diagnostic pop
 
+// acc + lo + hi of a packed bf16 pair, in float32 (v_dot2_f32_bf16 against
+// (1, 1)), so the row sums use exactly the rounded probabilities of the P.V
+// product.  The VOP3P form is written out: the accumulate-in-place VOP2 form
+// (v_dot2c_f32_bf16) read wrong values on gfx950 right after the
+// v_cvt_pk_bf16_f32 that produced its operand, and the builtin lowers to it.
+__device__ __forceinline__ float sum_bf16_pair(float acc, unsigned int pair) {
+  const unsigned int ones = 0x3F803F80u;
+  float r;
+  asm("v_dot2_f32_bf16 %0, %1, %2, %3" : "=v"(r) : "v"(pair), "v"(ones), "v"(acc));
+  return r;
+}
+
 template <int S>
 struct Stage {
   static constexpr int value = S;
@@ -245,7 +257,7 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_d64(AttnArgs a) {
     }
     float mx = fmaxf(sc[0][0], sc[1][0]);
 #pragma unroll
-    for (int e = 1; e < 16; ++e) mx = fmaxf(mx, fmaxf(sc[0][e], sc[1][e]));
+    for (int e = 1; e < 16; ++e) mx = fmaxf(fmaxf(mx, sc[0][e]), sc[1][e]);  // v_max3 chain
     const float mt = swap_max(mx);  // tile max relative to m_ref
     if (t == t_begin || __builtin_amdgcn_ballot_w64(mt > kRescale)) {
       // Move the reference: on the first tile to the tile max (o and l are
@@ -278,11 +290,11 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_d64(AttnArgs a) {
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
         pb[blk][s2] = pack8(sc[blk], 8 * s2);
-#pragma unroll
-        for (int j = 0; j < 8; j += 2) {
-          ls0 += sc[blk][8 * s2 + j];
-          ls1 += sc[blk][8 * s2 + j + 1];
-        }
+        const u32x4 w = __builtin_bit_cast(u32x4, pb[blk][s2]);
+        ls0 = sum_bf16_pair(ls0, w[0]);
+        ls1 = sum_bf16_pair(ls1, w[1]);
+        ls0 = sum_bf16_pair(ls0, w[2]);
+        ls1 = sum_bf16_pair(ls1, w[3]);
       }
     }
     l_part += ls0 + ls1;
