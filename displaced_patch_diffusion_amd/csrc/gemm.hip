@@ -10,18 +10,30 @@
 // Reduction index of the conv: k = tap * Cin + c with tap = (dy+1)*3 + (dx+1),
 // matching the [Cout, 3, 3, Cin] weight layout, so weight rows are K-contiguous.
 //
-// bf16 path (gfx950): 128x128 output tile per 256-thread block, K staged
-// through LDS in 64-wide slices (double-buffered, one barrier per slice).
-// Each wave owns a 64x64 sub-tile computed with v_mfma_f32_32x32x16_bf16 as
-// (W rows) x (A rows)^T, so an accumulator lane holds 4 consecutive output
-// channels of one output row and the epilogue writes 8-byte runs.
+// bf16 path (gfx950): a 256-thread block computes a 128x128, 128x64, 64x128 or
+// 64x64 output tile (chosen per problem so the tiles spread evenly over the
+// CUs); tiles sharing A rows are dealt to one XCD.  K moves through a 3-stage
+// LDS ring in 32-wide slices by direct global->LDS loads (two slices ahead),
+// 64-byte rows XOR-swizzled.  Each wave owns a quarter of the tile as
+// v_mfma_f32_32x32x16_bf16 blocks computed as (W rows) x (A rows)^T, so an
+// accumulator lane holds 4 consecutive output channels of one output row and
+// the epilogue writes 8-byte runs.
 // f32 path: a plain LDS-tiled FMA kernel (correctness path for fp32 shares).
+#include <cmath>
+
 #include "dp_internal.h"
 
 namespace {
 
-constexpr int kBM = 128, kBN = 128, kBK = 64, kPad = 8, kLd = kBK + kPad;
 constexpr int kThreads = 256;
+constexpr int kBK = 32;            // reduction slice (64 bytes of bf16 per row)
+constexpr int kStages = 3;         // LDS ring depth (loads run two slices ahead)
+constexpr int kXcds = 8;
+
+// Zero page read by padding rows of the implicit im2col (columns outside the
+// image, rows beyond a NULL halo, rows past M).  Such rows are re-pointed at
+// the page at every tap and advance at most Cin*2 <= 4096 bytes within it.
+__device__ __attribute__((aligned(256))) unsigned char g_zero_page[4096 + 256];
 
 struct ConvGeom {
   const bf16_t* x;
@@ -30,144 +42,280 @@ struct ConvGeom {
   int h, W, Cin;
 };
 
-template <bool CONV>
-__global__ void __launch_bounds__(kThreads, 2)
-gemm_bf16_mfma(const bf16_t* __restrict__ a, ConvGeom geo, const bf16_t* __restrict__ wt,
-               const float* __restrict__ bias, bf16_t* __restrict__ y, int M, int N, int K) {
-  __shared__ __attribute__((aligned(16))) bf16_t As[2][kBM * kLd];
-  __shared__ __attribute__((aligned(16))) bf16_t Bs[2][kBN * kLd];
+struct GemmArgs {
+  const bf16_t* a;     // dense rows [M, K] (projections)
+  ConvGeom geo;        // implicit im2col (conv)
+  const bf16_t* wt;    // [N, K]
+  const float* bias;   // [N] or null
+  bf16_t* y;           // [M, N]
+  int M, N, K;
+  int tiles_m, tiles_n, units, units_per_xcd;
+};
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int wn = wave & 1, wm = wave >> 1;
-  const int l32 = lane & 31, g = lane >> 5;
-  const int n0 = blockIdx.x * kBN, m0 = blockIdx.y * kBM;
+// 64-byte LDS rows: 16-byte chunk c of row r lives in slot c ^ ((r >> 2) & 3),
+// which keeps the operand reads (16 consecutive rows, one chunk) and the DMA
+// writes free of bank conflicts.
+__device__ __forceinline__ int gswz(int row) { return (row >> 2) & 3; }
 
-  // Global->LDS assignment: 16-byte chunk kc of rows r_u = (tid>>3) + 32u.
-  const int kc = tid & 7;
-  const int rbase = tid >> 3;
-  int am_b[4], am_i[4], am_c[4];
-  bool am_ok[4], wn_ok[4];
-  int64_t a_row_off[4];
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"  // m0 is written on purpose; nothing else here uses it
+// 16 bytes per lane straight into LDS at M0 + 16*lane (global_load_lds_dwordx4),
+// issued as inline assembly so completion is tracked only by the explicit
+// vmcnt waits of the k loop (compiler-inserted waits can only over-wait).
+__device__ __forceinline__ void gdma16(const void* gsrc, unsigned int m0) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+               :
+               : "s"(m0), "v"(gsrc)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N == 0 || N == 2 || N == 3 || N == 4, "vmcnt");
+  if constexpr (N == 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+  else if constexpr (N == 3) asm volatile("s_waitcnt vmcnt(3)" ::: "memory");
+  else if constexpr (N == 2) asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+  else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+template <int S>
+struct Stage {
+  static constexpr int value = S;
+};
+
+// One block computes a BM x BN output tile with 4 waves arranged 2 x 2; each
+// wave owns (BM/2) x (BN/2) as 32 x 32 MFMA blocks computed as (W rows) x
+// (A rows)^T, so an accumulator lane holds 4 consecutive output channels of one
+// output row.  K advances in 32-wide slices through a 3-stage LDS ring.
+template <int BM, int BN, bool CONV>
+__global__ void __launch_bounds__(kThreads, 2) gemm_bf16(GemmArgs g) {
+  constexpr int kABytes = BM * kBK * 2, kBBytes = BN * kBK * 2;
+  constexpr int kStageBytes = kABytes + kBBytes;
+  constexpr int kASlabs = BM / 64, kBSlabs = BN / 64;  // 1 KB DMA slabs per wave
+  constexpr int kDma = kASlabs + kBSlabs;              // DMA instructions per slice per wave
+  constexpr int WM = BM / 2, WN = BN / 2, MB = WM / 32, NB = WN / 32;
+  __shared__ __attribute__((aligned(1024))) char lds[kStages * kStageBytes];
+
+  const int u = (blockIdx.x % kXcds) * g.units_per_xcd + blockIdx.x / kXcds;
+  if (u >= g.units) return;
+  const int tn = u % g.tiles_n, tm = u / g.tiles_n;  // tiles sharing A rows stay on one XCD
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int l32 = lane & 31, gq = lane >> 5;
+
+  // ---- DMA addressing: slab j of this wave covers rows 16*(4*j + wave) + lane/4,
+  // lane l writes slot l%4 of its row, i.e. data chunk (l%4) ^ gswz(row).
+  const unsigned int lds0 = __builtin_amdgcn_readfirstlane(
+      static_cast<unsigned int>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)lds)) +
+      wave * 1024);
+  const char* bsrc[kBSlabs];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int m = m0 + rbase + 32 * u;
-    am_ok[u] = m < M;
-    wn_ok[u] = (n0 + rbase + 32 * u) < N;
+  for (int j = 0; j < kBSlabs; ++j) {
+    const int row = 16 * (4 * j + wave) + (lane >> 2);
+    const int chunk = (lane & 3) ^ gswz(row);
+    const int n = min(n0 + row, g.N - 1);  // rows past N repeat the last one; never stored
+    bsrc[j] = reinterpret_cast<const char*>(g.wt + static_cast<int64_t>(n) * g.K) + chunk * 16;
+  }
+  const char* asrc[kASlabs];
+  int a_b[kASlabs], a_i[kASlabs], a_c[kASlabs], a_chunk[kASlabs];
+  bool a_ok[kASlabs];
+#pragma unroll
+  for (int j = 0; j < kASlabs; ++j) {
+    const int row = 16 * (4 * j + wave) + (lane >> 2);
+    a_chunk[j] = (lane & 3) ^ gswz(row);
+    const int m = m0 + row;
+    a_ok[j] = m < g.M;
     if constexpr (CONV) {
-      const int hw = geo.h * geo.W;
-      const int mm = am_ok[u] ? m : 0;
-      am_b[u] = mm / hw;
-      const int rem = mm - am_b[u] * hw;
-      am_i[u] = rem / geo.W;
-      am_c[u] = rem - am_i[u] * geo.W;
-      a_row_off[u] = 0;
+      const int hw = g.geo.h * g.geo.W;
+      const int mm = a_ok[j] ? m : 0;
+      a_b[j] = mm / hw;
+      const int rem = mm - a_b[j] * hw;
+      a_i[j] = rem / g.geo.W;
+      a_c[j] = rem - a_i[j] * g.geo.W;
+      asrc[j] = nullptr;
     } else {
-      a_row_off[u] = static_cast<int64_t>(m) * K;
-      am_b[u] = am_i[u] = am_c[u] = 0;
+      a_b[j] = a_i[j] = a_c[j] = 0;  // rows past M repeat the last one; never stored
+      asrc[j] = reinterpret_cast<const char*>(g.a + static_cast<int64_t>(min(m, g.M - 1)) * g.K) + a_chunk[j] * 16;
     }
   }
-
-  const int n_kt = K / kBK;
-  const int kpt = CONV ? geo.Cin / kBK : 1;  // k-slices per conv tap
-  u32x4 ra[4], rw[4];
-
-  auto load_tile = [&](int kt) {
-    const int kofs = kt * kBK + kc * 8;
+  // conv: point the A rows at the source pixel of tap `tap` (channel 0), or the zero page
+  auto conv_rows = [&](int tap) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      // activations
+    for (int j = 0; j < kASlabs; ++j) {
+      const int dy = tap / 3 - 1, dx = tap % 3 - 1;
+      const int row = a_i[j] + dy, col = a_c[j] + dx;
       const bf16_t* src = nullptr;
-      if (am_ok[u]) {
-        if constexpr (CONV) {
-          const int tap = kt / kpt;
-          const int c0 = (kt - tap * kpt) * kBK + kc * 8;
-          const int dy = tap / 3 - 1, dx = tap % 3 - 1;
-          const int row = am_i[u] + dy, col = am_c[u] + dx;
-          if (col >= 0 && col < geo.W) {
-            if (row < 0) {
-              if (geo.halo_top)
-                src = geo.halo_top + (static_cast<int64_t>(am_b[u]) * geo.W + col) * geo.Cin + c0;
-            } else if (row >= geo.h) {
-              if (geo.halo_bot)
-                src = geo.halo_bot + (static_cast<int64_t>(am_b[u]) * geo.W + col) * geo.Cin + c0;
-            } else {
-              src = geo.x + ((static_cast<int64_t>(am_b[u]) * geo.h + row) * geo.W + col) * geo.Cin + c0;
-            }
-          }
+      if (a_ok[j] && col >= 0 && col < g.geo.W) {
+        if (row < 0) {
+          if (g.geo.halo_top) src = g.geo.halo_top + (static_cast<int64_t>(a_b[j]) * g.geo.W + col) * g.geo.Cin;
+        } else if (row >= g.geo.h) {
+          if (g.geo.halo_bot) src = g.geo.halo_bot + (static_cast<int64_t>(a_b[j]) * g.geo.W + col) * g.geo.Cin;
         } else {
-          src = a + a_row_off[u] + kofs;
+          src = g.geo.x + ((static_cast<int64_t>(a_b[j]) * g.geo.h + row) * g.geo.W + col) * g.geo.Cin;
         }
       }
-      ra[u] = src ? *reinterpret_cast<const u32x4*>(src) : u32x4{0u, 0u, 0u, 0u};
-      // weights
-      const int n = n0 + rbase + 32 * u;
-      rw[u] = wn_ok[u] ? *reinterpret_cast<const u32x4*>(wt + static_cast<int64_t>(n) * K + kofs)
-                       : u32x4{0u, 0u, 0u, 0u};
-    }
-  };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int r = rbase + 32 * u;
-      *reinterpret_cast<u32x4*>(&As[buf][r * kLd + kc * 8]) = ra[u];
-      *reinterpret_cast<u32x4*>(&Bs[buf][r * kLd + kc * 8]) = rw[u];
+      asrc[j] = (src ? reinterpret_cast<const char*>(src) : reinterpret_cast<const char*>(g_zero_page)) +
+                a_chunk[j] * 16;
     }
   };
 
-  f32x16 acc[2][2];
+  const int n_kt = g.K / kBK;
+  const int kpt = CONV ? g.geo.Cin / kBK : n_kt;  // slices per conv tap
+  // Issues slice kt into stage st: A slabs then B slabs; pointers advance one
+  // slice (64 bytes) per issue, and conv rows are re-pointed at each tap.
+  int tap_next = 0, in_tap = 0;
+  auto issue = [&](int st) {
+    if constexpr (CONV) {
+      if (in_tap == 0) conv_rows(tap_next);
+    }
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+    for (int j = 0; j < kASlabs; ++j) {
+      gdma16(asrc[j], lds0 + st * kStageBytes + j * 4096);
+      asrc[j] += kBK * 2;
+    }
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < kBSlabs; ++j) {
+      gdma16(bsrc[j], lds0 + st * kStageBytes + kABytes + j * 4096);
+      bsrc[j] += kBK * 2;
+    }
+    if constexpr (CONV) {
+      if (++in_tap == kpt) {
+        in_tap = 0;
+        ++tap_next;
+      }
+    }
+  };
+
+  // ---- operand offsets: A rows of this wave, W rows of this wave
+  int aoff[MB][2], boff[NB][2];
+#pragma unroll
+  for (int i = 0; i < MB; ++i)
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int row = wm * WM + 32 * i + l32;
+      aoff[i][s] = row * 64 + (((2 * s + gq) ^ gswz(row)) << 4);
+    }
+#pragma unroll
+  for (int i = 0; i < NB; ++i)
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int row = wn * WN + 32 * i + l32;
+      boff[i][s] = kABytes + row * 64 + (((2 * s + gq) ^ gswz(row)) << 4);
+    }
+
+  f32x16 acc[NB][MB];
+#pragma unroll
+  for (int i = 0; i < NB; ++i)
+#pragma unroll
+    for (int j = 0; j < MB; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-  for (int kt = 0; kt < n_kt; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < n_kt) load_tile(kt + 1);
+  auto step = [&](auto stage_c, int kt) {
+    constexpr int S = decltype(stage_c)::value;
+    if (kt + 1 < n_kt) wait_vm<kDma>();
+    else wait_vm<0>();
+    __syncthreads();  // slice kt visible; the stage of slice kt-1 is free
+    if (kt + 2 < n_kt) issue((S + 2) % 3);
 #pragma unroll
-    for (int s = 0; s < kBK / 16; ++s) {
-      bf16x8 wa[2], xb[2];
+    for (int s = 0; s < 2; ++s) {
+      bf16x8 wa[NB], xb[MB];
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb)
-        wa[nb] = *reinterpret_cast<const bf16x8*>(
-            &Bs[cur][(wn * 64 + nb * 32 + l32) * kLd + s * 16 + g * 8]);
+      for (int i = 0; i < NB; ++i) wa[i] = *reinterpret_cast<const bf16x8*>(lds + S * kStageBytes + boff[i][s]);
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-        xb[mb] = *reinterpret_cast<const bf16x8*>(
-            &As[cur][(wm * 64 + mb * 32 + l32) * kLd + s * 16 + g * 8]);
+      for (int j = 0; j < MB; ++j) xb[j] = *reinterpret_cast<const bf16x8*>(lds + S * kStageBytes + aoff[j][s]);
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb)
+      for (int i = 0; i < NB; ++i)
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-          acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wa[nb], xb[mb], acc[nb][mb], 0, 0, 0);
+        for (int j = 0; j < MB; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wa[i], xb[j], acc[i][j], 0, 0, 0);
     }
-    if (kt + 1 < n_kt) store_tile(cur ^ 1);
-    __syncthreads();
+  };
+
+  issue(0);
+  if (n_kt > 1) issue(1);
+  for (int kt = 0; kt < n_kt; kt += 3) {
+    step(Stage<0>{}, kt);
+    if (kt + 1 < n_kt) step(Stage<1>{}, kt + 1);
+    if (kt + 2 < n_kt) step(Stage<2>{}, kt + 2);
   }
 
-  // Epilogue: lane holds rows n = 8*(e/4) + 4*g + e%4 of column m = l32.
+  // Epilogue: lane holds rows n = 8*(e/4) + 4*gq + e%4 of column m = l32.
 #pragma unroll
-  for (int nb = 0; nb < 2; ++nb)
+  for (int i = 0; i < NB; ++i)
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-      const int m = m0 + wm * 64 + mb * 32 + l32;
-      const int nblk = n0 + wn * 64 + nb * 32;
-      if (m >= M || nblk >= N) continue;
+    for (int j = 0; j < MB; ++j) {
+      const int m = m0 + wm * WM + 32 * j + l32;
+      const int nblk = n0 + wn * WN + 32 * i;
+      if (m >= g.M || nblk >= g.N) continue;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int n = nblk + 8 * q + 4 * g;
+        const int n = nblk + 8 * q + 4 * gq;
         float v[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = acc[nb][mb][4 * q + e] + (bias ? bias[n + e] : 0.f);
+        for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * q + e] + (g.bias ? g.bias[n + e] : 0.f);
         u32x2 packed = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-        *reinterpret_cast<u32x2*>(y + static_cast<int64_t>(m) * N + n) = packed;
+        *reinterpret_cast<u32x2*>(g.y + static_cast<int64_t>(m) * g.N + n) = packed;
       }
     }
+}
+
+int gemm_cus() {
+  static thread_local int cached_dev = -1, cached = 256;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return 256;
+  }
+  if (dev != cached_dev) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && cus > 0)
+      cached = cus;
+    else
+      (void)hipGetLastError();
+    cached_dev = dev;
+  }
+  return cached;
+}
+
+template <int BM, int BN, bool CONV>
+void launch_bf16(const GemmArgs& base, hipStream_t st) {
+  GemmArgs g = base;
+  g.tiles_m = (g.M + BM - 1) / BM;
+  g.tiles_n = (g.N + BN - 1) / BN;
+  g.units = g.tiles_m * g.tiles_n;
+  g.units_per_xcd = (g.units + kXcds - 1) / kXcds;
+  hipLaunchKernelGGL((gemm_bf16<BM, BN, CONV>), dim3(static_cast<unsigned>(g.units_per_xcd * kXcds)),
+                     dim3(kThreads), 0, st, g);
+}
+
+// Tile shape: fewest tile-rounds per CU, weighting smaller tiles by their
+// higher LDS traffic per MFMA (measured relative cost per output element).
+template <bool CONV>
+void launch_bf16_auto(const GemmArgs& g, hipStream_t st) {
+  const int cus = gemm_cus();
+  struct Cand { int bm, bn; double cost_per_elem; };
+  const Cand cands[] = {{128, 128, 1.0}, {128, 64, 1.15}, {64, 128, 1.15}, {64, 64, 1.6}};
+  int best = 0;
+  double best_cost = 1e300;
+  for (int c = 0; c < 4; ++c) {
+    const int64_t tiles = static_cast<int64_t>((g.M + cands[c].bm - 1) / cands[c].bm) *
+                          ((g.N + cands[c].bn - 1) / cands[c].bn);
+    const double per_cu = std::ceil(static_cast<double>(tiles) / cus);
+    const double cost = per_cu * cands[c].bm * cands[c].bn * cands[c].cost_per_elem;
+    if (cost < best_cost * 0.999) {
+      best_cost = cost;
+      best = c;
+    }
+  }
+  switch (best) {
+    case 0: launch_bf16<128, 128, CONV>(g, st); break;
+    case 1: launch_bf16<128, 64, CONV>(g, st); break;
+    case 2: launch_bf16<64, 128, CONV>(g, st); break;
+    default: launch_bf16<64, 64, CONV>(g, st); break;
+  }
 }
 
 // ------------------------------------------------------------------ f32 path
@@ -243,21 +391,22 @@ dp_status run_gemm(bool conv, const void* a, const void* x, const void* ht, cons
     return dp::fail(DP_ERR_UNSUPPORTED, "%s: dimension exceeds 2^31", name);
   dp::clear_error();
   if (dt == DP_BF16) {
-    if (K % kBK != 0 || N % 32 != 0 || (conv && Cin % kBK != 0))
-      return dp::fail(DP_ERR_UNSUPPORTED, "%s: bf16 path needs Cin %% 64 == 0 and Cout %% 32 == 0", name);
-    const int64_t gy = (M + kBM - 1) / kBM;
-    if (gy > 65535) return dp::fail(DP_ERR_UNSUPPORTED, "%s: M too large", name);
-    const dim3 grid(static_cast<unsigned>((N + kBN - 1) / kBN), static_cast<unsigned>(gy));
-    ConvGeom geo{static_cast<const bf16_t*>(x), static_cast<const bf16_t*>(ht),
-                 static_cast<const bf16_t*>(hb), h, W, Cin};
-    if (conv)
-      hipLaunchKernelGGL(gemm_bf16_mfma<true>, grid, dim3(kThreads), 0, st, nullptr, geo,
-                         static_cast<const bf16_t*>(wt), bias, static_cast<bf16_t*>(y), (int)M,
-                         (int)N, (int)K);
-    else
-      hipLaunchKernelGGL(gemm_bf16_mfma<false>, grid, dim3(kThreads), 0, st,
-                         static_cast<const bf16_t*>(a), geo, static_cast<const bf16_t*>(wt), bias,
-                         static_cast<bf16_t*>(y), (int)M, (int)N, (int)K);
+    if (K % kBK != 0 || N % 32 != 0 || (conv && (Cin % kBK != 0 || Cin > 2048)))
+      return dp::fail(DP_ERR_UNSUPPORTED, "%s: bf16 path needs Cin %% 32 == 0 (conv: Cin <= 2048) and Cout %% 32 == 0", name);
+    if ((M + 63) / 64 * ((N + 63) / 64) > 0x3FFFFFFF)
+      return dp::fail(DP_ERR_UNSUPPORTED, "%s: too many tiles", name);
+    GemmArgs g{};
+    g.a = static_cast<const bf16_t*>(a);
+    g.geo = ConvGeom{static_cast<const bf16_t*>(x), static_cast<const bf16_t*>(ht),
+                     static_cast<const bf16_t*>(hb), h, W, Cin};
+    g.wt = static_cast<const bf16_t*>(wt);
+    g.bias = bias;
+    g.y = static_cast<bf16_t*>(y);
+    g.M = (int)M;
+    g.N = (int)N;
+    g.K = (int)K;
+    if (conv) launch_bf16_auto<true>(g, st);
+    else launch_bf16_auto<false>(g, st);
   } else {
     const int64_t gy = (M + kFT - 1) / kFT;
     if (gy > 65535) return dp::fail(DP_ERR_UNSUPPORTED, "%s: M too large", name);

@@ -108,7 +108,8 @@ dp_status dp_attn_stale_kv(const void* q, const void* k_buf, const void* v_buf, 
  *
  * x [B, h, W, Cin]; halo_top, halo_bot [B, W, Cin] or NULL (an image edge:
  * zeros); w [Cout, 3, 3, Cin]; bias [Cout] float32 or NULL; y [B, h, W, Cout].
- * Supported: bf16 with Cin % 64 == 0 and Cout % 32 == 0 (MFMA path); f32 any size.
+ * Supported: bf16 with Cin % 32 == 0, Cin <= 2048 and Cout % 32 == 0 (MFMA path);
+ * f32 any size.
  * Errors: INVALID_ARG for NULL x/w/y or sizes <= 0; UNSUPPORTED otherwise.
  */
 dp_status dp_conv3x3_stale_halo(const void* x, const void* halo_top, const void* halo_bot,
@@ -150,7 +151,7 @@ dp_status dp_groupnorm_stale_stats(const void* x, const float* stale_sums, int64
  * stale rows are never recomputed):
  *   y[m, o] = sum_c x[m, c] * w[o, c] (+ bias[o])
  * x [M, Cin]; w [Cout, Cin]; bias [Cout] float32 or NULL; y [M, Cout].
- * Supported: bf16 with Cin % 64 == 0 and Cout % 32 == 0; f32 any size.
+ * Supported: bf16 with Cin % 32 == 0 and Cout % 32 == 0; f32 any size.
  * Errors: INVALID_ARG for NULL x/w/y or sizes <= 0; UNSUPPORTED otherwise.
  */
 dp_status dp_linear(const void* x, const void* w, const float* bias, void* y, int64_t M,

@@ -94,7 +94,7 @@ def test_conv_and_linear_validation(lib):
     st, _ = status_and_error(lib.dp_conv3x3_stale_halo, A, None, None, Bp, None, Cp, 2, 0, 8, 64, 64,
                              _lib.DP_BF16, None)
     assert st == _lib.DP_ERR_INVALID_ARG
-    st, _ = status_and_error(lib.dp_linear, A, Bp, None, Cp, 100, 40, 64, _lib.DP_BF16, None)
+    st, _ = status_and_error(lib.dp_linear, A, Bp, None, Cp, 100, 48, 64, _lib.DP_BF16, None)
     assert st == _lib.DP_ERR_UNSUPPORTED
     st, _ = status_and_error(lib.dp_linear, A, Bp, None, Cp, -1, 64, 64, _lib.DP_BF16, None)
     assert st == _lib.DP_ERR_INVALID_ARG

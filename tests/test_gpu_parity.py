@@ -52,6 +52,7 @@ def test_splice_bit_exact(dt, B, T_kv, C, t0, T_loc):
 # --------------------------------------------------------------------- linear
 @pytest.mark.parametrize("dt,M,Cin,Cout,bias", [
     ("bf16", 300, 128, 96, True), ("bf16", 1024, 640, 640, False), ("bf16", 129, 64, 32, True),
+    ("bf16", 8192, 640, 640, True), ("bf16", 200, 2560, 96, False), ("bf16", 77, 32, 352, True),
     ("f32", 300, 64, 64, True), ("f32", 77, 50, 30, False),
 ])
 def test_linear(dt, M, Cin, Cout, bias):
@@ -67,6 +68,7 @@ def test_linear(dt, M, Cin, Cout, bias):
 @pytest.mark.parametrize("dt,B,h,W,Cin,Cout,halos", [
     ("bf16", 2, 5, 9, 64, 64, "both"), ("bf16", 1, 3, 40, 128, 96, "top"),
     ("bf16", 2, 1, 7, 64, 32, "bottom"), ("bf16", 2, 4, 33, 64, 160, "none"),
+    ("bf16", 2, 3, 50, 96, 320, "both"), ("bf16", 1, 2, 200, 32, 64, "top"),
     ("f32", 2, 16, 32, 64, 64, "both"), ("f32", 1, 2, 5, 6, 7, "top"),
 ])
 def test_conv3x3(dt, B, h, W, Cin, Cout, halos):
