@@ -6,236 +6,258 @@
 // contrast) and the xDiT issue thread "Tensor Parallelism with Stale
 // Activations ..." (a feature may combine fresh partial values with stale ones).
 //
-// Three HBM-streaming passes, all deterministic (fixed reduction order, no
-// float atomics):
-//   1. gn_partial:  per (batch, token tile) per-group (sum x, sum x^2)
-//   2. gn_finalize: per batch, fold the tiles in order, write the fresh local
-//                   sums, add the other patches' stale sums, derive mean/rstd
-//   3. gn_apply:    y = x * a_c + b_c (a_c = rstd*gamma, b_c = beta - mean*a_c),
-//                   optional SiLU, written in the storage type
+// Two launches over the same (token tile, batch item) grid, deterministic
+// (fixed reduction order, no float atomics, no inter-block waiting):
+//   1. gn_partial: per tile, per group (sum x, sum x^2) -> workspace
+//   2. gn_apply:   every block folds the partials of its batch item in a fixed
+//                  order (so all blocks derive bit-identical statistics), adds
+//                  the other patches' stale sums, derives a_c = rstd*gamma_c and
+//                  b_c = beta_c - mean*a_c, then writes y = x*a_c + b_c (optional
+//                  SiLU) for its tile; the tile of block (0, b) also writes the
+//                  fresh local sums.
+// Both launches use the same block -> tile mapping, so the tile that block i
+// re-reads in pass 2 was read by block i -- on the same XCD -- in pass 1.
 // Every thread owns one 16-byte channel vector of a token, so loads and stores
 // are 16 B wide and consecutive threads touch consecutive bytes.
 #include "dp_internal.h"
 
 namespace {
 
-constexpr int kMaxThreads = 256;
+constexpr int kThreads = 512;
+constexpr int kTargetBlocks = 512;  // about two blocks per CU
+constexpr int kUnroll = 8;          // 16-byte loads in flight per thread
 
-struct GnPlan {
-  int vec;          // channels per 16-byte vector
-  int vpt;          // vectors per token
-  int tpp;          // tokens per pass of one block
-  int threads;      // tpp * vpt
-  int tile_tokens;  // tokens per block
-  int tiles;        // blocks per batch item
+struct GnArgs {
+  const void* x;
+  void* y;
+  float2* partial;      // [B][tiles][G]
+  const float* stale;   // [n_patches][B][G][2]
+  const float* gamma;
+  const float* beta;
+  float* fresh;         // [B][G][2] or NULL
+  int T, C, G, tiles, tile_tokens, n_patches, rank, B, silu;
+  float inv_count, eps;
 };
 
-// Tiling depends on (B, T, C) only, so the workspace size does not depend on
-// the dtype.
-void tiles_for(int64_t B, int64_t T, int& tile_tokens, int& tiles) {
-  int64_t tt = (T * B + 1023) / 1024;
-  if (tt < 16) tt = 16;
-  if (tt > T) tt = T;
-  tile_tokens = static_cast<int>(tt);
-  tiles = static_cast<int>((T + tt - 1) / tt);
+// Upper bound of tiles per batch item, independent of C and dtype (it sizes
+// the workspace).
+int64_t max_tiles(int64_t B, int64_t T) {
+  const int64_t want = (kTargetBlocks + B - 1) / B;
+  return want < T ? want : T;
 }
 
+struct GnPlan {
+  int tpp, tile_tokens, tiles;
+};
+
 GnPlan make_plan(int64_t B, int64_t T, int64_t C, dp_dtype dt) {
+  const int vec = dt == DP_BF16 ? 8 : 4;
+  const int vpt = static_cast<int>(C / vec);
   GnPlan p;
-  p.vec = dt == DP_BF16 ? 8 : 4;
-  p.vpt = static_cast<int>(C / p.vec);
-  p.tpp = kMaxThreads / p.vpt;
-  p.threads = p.tpp * p.vpt;
-  tiles_for(B, T, p.tile_tokens, p.tiles);
+  p.tpp = kThreads / vpt;
+  const int64_t t0 = max_tiles(B, T);
+  int64_t tt = (T + t0 - 1) / t0;
+  tt = (tt + p.tpp - 1) / p.tpp * p.tpp;  // whole passes of the block
+  p.tile_tokens = static_cast<int>(tt);
+  p.tiles = static_cast<int>((T + tt - 1) / tt);  // <= t0
   return p;
 }
 
 template <bool BF16>
-__device__ __forceinline__ void load_vec(const void* base, int64_t elem, float* v) {
+__device__ __forceinline__ void unpack_vec(const u32x4& u, float* v) {
   if constexpr (BF16) {
-    const u32x4 u = *reinterpret_cast<const u32x4*>(static_cast<const bf16_t*>(base) + elem);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       v[2 * j] = bf16_lo(u[j]);
       v[2 * j + 1] = bf16_hi(u[j]);
     }
   } else {
-    const f32x4 u = *reinterpret_cast<const f32x4*>(static_cast<const float*>(base) + elem);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) v[j] = u[j];
+    for (int j = 0; j < 4; ++j) v[j] = __uint_as_float(u[j]);
   }
 }
 
 template <bool BF16>
-__device__ __forceinline__ void store_vec(void* base, int64_t elem, const float* v) {
+__device__ __forceinline__ u32x4 pack_vec(const float* v) {
+  u32x4 u;
   if constexpr (BF16) {
-    u32x4 u;
 #pragma unroll
     for (int j = 0; j < 4; ++j) u[j] = pack_bf16x2(v[2 * j], v[2 * j + 1]);
-    *reinterpret_cast<u32x4*>(static_cast<bf16_t*>(base) + elem) = u;
   } else {
-    f32x4 u;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) u[j] = v[j];
-    *reinterpret_cast<f32x4*>(static_cast<float*>(base) + elem) = u;
+    for (int j = 0; j < 4; ++j) u[j] = __float_as_uint(v[j]);
   }
+  return u;
 }
 
-// partial[(b*tiles + tile)*G + g][2] = (sum x, sum x^2) over the tile's tokens.
+// Byte offset of the 16-byte vector vi of token t of batch item b.
 template <bool BF16>
-__global__ void __launch_bounds__(kMaxThreads)
-gn_partial(const void* __restrict__ x, float* __restrict__ partial, int T, int C, int G,
-           int tile_tokens, int tiles) {
+__device__ __forceinline__ int64_t vec_byte(int b, int t, int vi, const GnArgs& a) {
+  return ((static_cast<int64_t>(b) * a.T + t) * a.C) * (BF16 ? 2 : 4) + static_cast<int64_t>(vi) * 16;
+}
+
+template <bool BF16>
+__global__ void __launch_bounds__(kThreads) gn_partial(GnArgs a) {
   constexpr int VEC = BF16 ? 8 : 4;
-  extern __shared__ float lds[];  // [2][tpp][C], then [2][C]
-  const int vpt = C / VEC;
-  const int tpp = blockDim.x / vpt;
-  const int tl = threadIdx.x / vpt, vi = threadIdx.x % vpt;
+  __shared__ float r[2][kThreads * VEC];  // [tpp][C] per statistic
+  __shared__ float csum[2][2048];
+  const int vpt = a.C / VEC, tpp = kThreads / vpt;
+  const int tid = threadIdx.x, tl = tid / vpt, vi = tid % vpt;
+  const bool active = tl < tpp;
   const int b = blockIdx.y, tile = blockIdx.x;
-  const int t_begin = tile * tile_tokens;
-  const int t_end = min(T, t_begin + tile_tokens);
+  const int t_begin = tile * a.tile_tokens;
+  const int t_end = min(a.T, t_begin + a.tile_tokens);
+  const int npass = a.tile_tokens / tpp;
+  const char* xb = static_cast<const char*>(a.x);
 
   float s1[VEC], s2[VEC];
 #pragma unroll
   for (int j = 0; j < VEC; ++j) s1[j] = s2[j] = 0.f;
-  const int64_t row0 = static_cast<int64_t>(b) * T;
-  for (int t = t_begin + tl; t < t_end; t += tpp) {
-    float v[VEC];
-    load_vec<BF16>(x, (row0 + t) * C + vi * VEC, v);
+  for (int k0 = 0; k0 < npass; k0 += kUnroll) {
+    u32x4 raw[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int t = t_begin + tl + (k0 + u) * tpp;
+      raw[u] = u32x4{0u, 0u, 0u, 0u};
+      if (active && k0 + u < npass && t < t_end)
+        raw[u] = *reinterpret_cast<const u32x4*>(xb + vec_byte<BF16>(b, t, vi, a));
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      float v[VEC];
+      unpack_vec<BF16>(raw[u], v);
+#pragma unroll
+      for (int j = 0; j < VEC; ++j) {
+        s1[j] += v[j];
+        s2[j] = fmaf(v[j], v[j], s2[j]);
+      }
+    }
+  }
+  if (active) {
 #pragma unroll
     for (int j = 0; j < VEC; ++j) {
-      s1[j] += v[j];
-      s2[j] = fmaf(v[j], v[j], s2[j]);
+      r[0][tl * a.C + vi * VEC + j] = s1[j];
+      r[1][tl * a.C + vi * VEC + j] = s2[j];
     }
   }
-  float* r1 = lds;
-  float* r2 = lds + tpp * C;
-#pragma unroll
-  for (int j = 0; j < VEC; ++j) {
-    r1[tl * C + vi * VEC + j] = s1[j];
-    r2[tl * C + vi * VEC + j] = s2[j];
-  }
   __syncthreads();
-  float* c1 = lds + 2 * tpp * C;
-  float* c2 = c1 + C;
-  for (int c = threadIdx.x; c < C; c += blockDim.x) {
-    float a = 0.f, q = 0.f;
+  for (int c = tid; c < a.C; c += kThreads) {  // per channel, token lanes in order
+    float p1 = 0.f, p2 = 0.f;
     for (int k = 0; k < tpp; ++k) {
-      a += r1[k * C + c];
-      q += r2[k * C + c];
+      p1 += r[0][k * a.C + c];
+      p2 += r[1][k * a.C + c];
     }
-    c1[c] = a;
-    c2[c] = q;
+    csum[0][c] = p1;
+    csum[1][c] = p2;
   }
   __syncthreads();
-  const int Cg = C / G;
-  for (int g = threadIdx.x; g < G; g += blockDim.x) {
-    float a = 0.f, q = 0.f;
+  const int Cg = a.C / a.G;
+  for (int g = tid; g < a.G; g += kThreads) {  // per group, channels in order
+    float p1 = 0.f, p2 = 0.f;
     for (int c = g * Cg; c < (g + 1) * Cg; ++c) {
-      a += c1[c];
-      q += c2[c];
+      p1 += csum[0][c];
+      p2 += csum[1][c];
     }
-    float* out = partial + ((static_cast<int64_t>(b) * tiles + tile) * G + g) * 2;
-    out[0] = a;
-    out[1] = q;
-  }
-}
-
-// One block per batch item.  stats[b][g] = (mean, rstd); fresh[b][g] = local sums.
-__global__ void __launch_bounds__(kMaxThreads)
-gn_finalize(const float* __restrict__ partial, const float* __restrict__ stale, int n_patches,
-            int rank, int B, int G, int tiles, float inv_count, float eps,
-            float* __restrict__ stats, float* __restrict__ fresh) {
-  __shared__ float red[2][kMaxThreads];
-  const int b = blockIdx.x;
-  // Threads sharing g = tid % G each fold a strided subset of the tiles.
-  const int lanes_per_g = G <= kMaxThreads ? kMaxThreads / G : 1;
-  for (int g0 = 0; g0 < G; g0 += kMaxThreads) {
-    const int span = min(G - g0, kMaxThreads);
-    const int per = G <= kMaxThreads ? lanes_per_g : 1;
-    const int gi = threadIdx.x % span;
-    const int part = threadIdx.x / span;
-    float a = 0.f, q = 0.f;
-    if (part < per) {
-      for (int t = part; t < tiles; t += per) {
-        const float* p = partial + ((static_cast<int64_t>(b) * tiles + t) * G + g0 + gi) * 2;
-        a += p[0];
-        q += p[1];
-      }
-    }
-    red[0][threadIdx.x] = a;
-    red[1][threadIdx.x] = q;
-    __syncthreads();
-    if (threadIdx.x < span) {
-      float s1 = 0.f, s2 = 0.f;
-      for (int k = 0; k < per; ++k) {
-        s1 += red[0][k * span + threadIdx.x];
-        s2 += red[1][k * span + threadIdx.x];
-      }
-      const int g = g0 + threadIdx.x;
-      if (fresh) {
-        fresh[(b * G + g) * 2 + 0] = s1;
-        fresh[(b * G + g) * 2 + 1] = s2;
-      }
-      for (int p = 0; p < n_patches; ++p) {
-        if (p == rank) continue;
-        s1 += stale[((static_cast<int64_t>(p) * B + b) * G + g) * 2 + 0];
-        s2 += stale[((static_cast<int64_t>(p) * B + b) * G + g) * 2 + 1];
-      }
-      const float mean = s1 * inv_count;
-      const float var = fmaxf(s2 * inv_count - mean * mean, 0.f);
-      stats[(b * G + g) * 2 + 0] = mean;
-      stats[(b * G + g) * 2 + 1] = 1.0f / sqrtf(var + eps);
-    }
-    __syncthreads();
+    a.partial[(static_cast<int64_t>(b) * a.tiles + tile) * a.G + g] = make_float2(p1, p2);
   }
 }
 
 template <bool BF16>
-__global__ void __launch_bounds__(kMaxThreads)
-gn_apply(const void* __restrict__ x, void* __restrict__ y, const float* __restrict__ stats,
-         const float* __restrict__ gamma, const float* __restrict__ beta, int T, int C, int G,
-         int tile_tokens, int silu) {
+__global__ void __launch_bounds__(kThreads) gn_apply(GnArgs a) {
   constexpr int VEC = BF16 ? 8 : 4;
-  const int vpt = C / VEC;
-  const int tpp = blockDim.x / vpt;
-  const int tl = threadIdx.x / vpt, vi = threadIdx.x % vpt;
-  const int b = blockIdx.y;
-  const int t_begin = blockIdx.x * tile_tokens;
-  const int t_end = min(T, t_begin + tile_tokens);
-  const int Cg = C / G;
-  float a[VEC], sh[VEC];
+  __shared__ float2 red[2048];      // [lanes][G], lanes * G <= max(G, kThreads)
+  __shared__ float2 gstat[2048];    // (mean, rstd) per group
+  const int tid = threadIdx.x;
+  const int b = blockIdx.y, tile = blockIdx.x;
+  const int G = a.G;
+
+  // ---- fold the partials of batch item b: lane q sums tiles q, q+lanes, ...
+  const int lanes = G >= kThreads ? 1 : kThreads / G;
+  const float2* pb = a.partial + static_cast<int64_t>(b) * a.tiles * G;
+  for (int f = tid; f < lanes * G; f += kThreads) {
+    const int g = f % G, q = f / G;
+    float2 s = make_float2(0.f, 0.f);
+    for (int t = q; t < a.tiles; t += lanes) {
+      const float2 p = pb[static_cast<int64_t>(t) * G + g];
+      s.x += p.x;
+      s.y += p.y;
+    }
+    red[f] = s;
+  }
+  __syncthreads();
+  for (int g = tid; g < G; g += kThreads) {
+    float f1 = 0.f, f2 = 0.f;
+    for (int q = 0; q < lanes; ++q) {
+      f1 += red[q * G + g].x;
+      f2 += red[q * G + g].y;
+    }
+    if (tile == 0 && a.fresh) {
+      a.fresh[(static_cast<int64_t>(b) * G + g) * 2 + 0] = f1;
+      a.fresh[(static_cast<int64_t>(b) * G + g) * 2 + 1] = f2;
+    }
+    for (int p = 0; p < a.n_patches; ++p) {
+      if (p == a.rank) continue;
+      const float* st = a.stale + ((static_cast<int64_t>(p) * a.B + b) * G + g) * 2;
+      f1 += st[0];
+      f2 += st[1];
+    }
+    const float mean = f1 * a.inv_count;
+    const float var = fmaxf(f2 * a.inv_count - mean * mean, 0.f);
+    gstat[g] = make_float2(mean, 1.0f / sqrtf(var + a.eps));
+  }
+  __syncthreads();
+
+  // ---- normalise the tile
+  const int vpt = a.C / VEC, tpp = kThreads / vpt;
+  const int tl = tid / vpt, vi = tid % vpt;
+  if (tl >= tpp) return;
+  const int Cg = a.C / G;
+  float ca[VEC], cb[VEC];
 #pragma unroll
   for (int j = 0; j < VEC; ++j) {
     const int c = vi * VEC + j;
-    const int g = c / Cg;
-    const float mean = stats[(b * G + g) * 2 + 0];
-    const float rstd = stats[(b * G + g) * 2 + 1];
-    const float gm = gamma ? gamma[c] : 1.f;
-    const float bt = beta ? beta[c] : 0.f;
-    a[j] = rstd * gm;
-    sh[j] = bt - mean * a[j];
+    const float2 ms = gstat[c / Cg];
+    const float gm = a.gamma ? a.gamma[c] : 1.f;
+    const float bt = a.beta ? a.beta[c] : 0.f;
+    ca[j] = ms.y * gm;
+    cb[j] = bt - ms.x * ca[j];
   }
-  const int64_t row0 = static_cast<int64_t>(b) * T;
-  for (int t = t_begin + tl; t < t_end; t += tpp) {
-    const int64_t e = (row0 + t) * C + vi * VEC;
-    float v[VEC];
-    load_vec<BF16>(x, e, v);
+  const int t_begin = tile * a.tile_tokens;
+  const int t_end = min(a.T, t_begin + a.tile_tokens);
+  const int npass = a.tile_tokens / tpp;
+  const char* xb = static_cast<const char*>(a.x);
+  char* yb = static_cast<char*>(a.y);
+  for (int k0 = 0; k0 < npass; k0 += kUnroll) {
+    u32x4 raw[kUnroll];
 #pragma unroll
-    for (int j = 0; j < VEC; ++j) {
-      float o = fmaf(v[j], a[j], sh[j]);
-      if (silu) o = o / (1.0f + __expf(-o));
-      v[j] = o;
+    for (int u = 0; u < kUnroll; ++u) {
+      const int t = t_begin + tl + (k0 + u) * tpp;
+      if (k0 + u < npass && t < t_end)
+        raw[u] = *reinterpret_cast<const u32x4*>(xb + vec_byte<BF16>(b, t, vi, a));
     }
-    store_vec<BF16>(y, e, v);
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int t = t_begin + tl + (k0 + u) * tpp;
+      if (k0 + u < npass && t < t_end) {
+        float v[VEC];
+        unpack_vec<BF16>(raw[u], v);
+#pragma unroll
+        for (int j = 0; j < VEC; ++j) {
+          float z = fmaf(v[j], ca[j], cb[j]);
+          if (a.silu) z = z / (1.0f + __expf(-z));
+          v[j] = z;
+        }
+        __builtin_nontemporal_store(pack_vec<BF16>(v),
+                                    reinterpret_cast<u32x4*>(yb + vec_byte<BF16>(b, t, vi, a)));
+      }
+    }
   }
 }
 
+// Workspace: the per-tile partials [B][max_tiles][G] of float2.
 size_t workspace_bytes(int64_t B, int64_t T, int64_t G) {
-  int tt, tiles;
-  tiles_for(B, T, tt, tiles);
-  return static_cast<size_t>(B) * (static_cast<size_t>(tiles) + 1) * static_cast<size_t>(G) * 2 *
-         sizeof(float);
+  return static_cast<size_t>(B) * static_cast<size_t>(max_tiles(B, T)) * static_cast<size_t>(G) *
+         sizeof(float2);
 }
 
 }  // namespace
@@ -272,7 +294,7 @@ DP_API dp_status dp_groupnorm_stale_stats(const void* x, const float* stale_sums
     return fail(DP_ERR_INVALID_ARG, "dp_groupnorm_stale_stats: workspace %zu < %zu bytes",
                 ws_bytes, need);
   const int vec = dt == DP_BF16 ? 8 : 4;
-  if (C % vec != 0 || C / vec > kMaxThreads || T_loc > 0x7FFFFFFF || B > 65535 || G > 65535 ||
+  if (C % vec != 0 || C > 2048 || C / vec > kThreads || T_loc > 0x7FFFFFFF || B > 65535 || G > 65535 ||
       B * G > 0x7FFFFFFF)
     return fail(DP_ERR_UNSUPPORTED, "dp_groupnorm_stale_stats: C=%lld G=%lld not supported",
                 (long long)C, (long long)G);
@@ -280,27 +302,33 @@ DP_API dp_status dp_groupnorm_stale_stats(const void* x, const float* stale_sums
   const size_t xb = static_cast<size_t>(B * T_loc * C) * es;
   if (dp::overlaps(x, xb, y, xb)) return fail(DP_ERR_INVALID_ARG, "dp_groupnorm_stale_stats: x and y overlap");
 
+  GnArgs ga;
   const GnPlan p = make_plan(B, T_loc, C, dt);
-  float* partial = static_cast<float*>(ws);
-  float* stats = partial + static_cast<size_t>(B) * p.tiles * G * 2;
-  const float inv_count = static_cast<float>(1.0 / (static_cast<double>(T_total) * (C / G)));
-  const size_t lds1 = (2 * static_cast<size_t>(p.tpp) * C + 2 * C) * sizeof(float);
-  dp::clear_error();
-  const dim3 grid(p.tiles, static_cast<unsigned>(B));
-  if (dt == DP_BF16)
-    hipLaunchKernelGGL(gn_partial<true>, grid, dim3(p.threads), lds1, stream, x, partial,
-                       (int)T_loc, (int)C, (int)G, p.tile_tokens, p.tiles);
-  else
-    hipLaunchKernelGGL(gn_partial<false>, grid, dim3(p.threads), lds1, stream, x, partial,
-                       (int)T_loc, (int)C, (int)G, p.tile_tokens, p.tiles);
-  hipLaunchKernelGGL(gn_finalize, dim3(static_cast<unsigned>(B)), dim3(kMaxThreads), 0, stream,
-                     partial, stale_sums, (int)n_patches, (int)rank, (int)B, (int)G, p.tiles,
-                     inv_count, eps, stats, fresh_sums_out);
-  if (dt == DP_BF16)
-    hipLaunchKernelGGL(gn_apply<true>, grid, dim3(p.threads), 0, stream, x, y, stats, gamma, beta,
-                       (int)T_loc, (int)C, (int)G, p.tile_tokens, fuse_silu);
-  else
-    hipLaunchKernelGGL(gn_apply<false>, grid, dim3(p.threads), 0, stream, x, y, stats, gamma, beta,
-                       (int)T_loc, (int)C, (int)G, p.tile_tokens, fuse_silu);
+  ga.x = x;
+  ga.y = y;
+  ga.partial = static_cast<float2*>(ws);
+  ga.stale = stale_sums;
+  ga.gamma = gamma;
+  ga.beta = beta;
+  ga.fresh = fresh_sums_out;
+  ga.T = static_cast<int>(T_loc);
+  ga.C = static_cast<int>(C);
+  ga.G = static_cast<int>(G);
+  ga.tiles = p.tiles;
+  ga.tile_tokens = p.tile_tokens;
+  ga.n_patches = static_cast<int>(n_patches);
+  ga.rank = static_cast<int>(rank);
+  ga.B = static_cast<int>(B);
+  ga.silu = fuse_silu;
+  ga.inv_count = static_cast<float>(1.0 / (static_cast<double>(T_total) * (C / G)));
+  ga.eps = eps;
+  const dim3 grid(static_cast<unsigned>(p.tiles), static_cast<unsigned>(B));
+  if (dt == DP_BF16) {
+    hipLaunchKernelGGL(gn_partial<true>, grid, dim3(kThreads), 0, stream, ga);
+    hipLaunchKernelGGL(gn_apply<true>, grid, dim3(kThreads), 0, stream, ga);
+  } else {
+    hipLaunchKernelGGL(gn_partial<false>, grid, dim3(kThreads), 0, stream, ga);
+    hipLaunchKernelGGL(gn_apply<false>, grid, dim3(kThreads), 0, stream, ga);
+  }
   return dp::check_launch("dp_groupnorm_stale_stats");
 }
