@@ -9,16 +9,25 @@
 // Two launches over the same (token tile, batch item) grid, deterministic
 // (fixed reduction order, no float atomics, no inter-block waiting):
 //   1. gn_partial: per tile, per group (sum x, sum x^2) -> workspace
-//   2. gn_apply:   every block folds the partials of its batch item in a fixed
-//                  order (so all blocks derive bit-identical statistics), adds
-//                  the other patches' stale sums, derives a_c = rstd*gamma_c and
-//                  b_c = beta_c - mean*a_c, then writes y = x*a_c + b_c (optional
-//                  SiLU) for its tile; the tile of block (0, b) also writes the
-//                  fresh local sums.
-// Both launches use the same block -> tile mapping, so the tile that block i
-// re-reads in pass 2 was read by block i -- on the same XCD -- in pass 1.
+//   2. gn_apply:   every block folds the partials of its batch item in one
+//                  fixed order (so all blocks derive bit-identical statistics),
+//                  adds the other patches' stale sums and writes
+//                  y = x * a_c + b_c (a_c = rstd*gamma_c, b_c = beta_c - mean*a_c,
+//                  optional SiLU) for its tile; the block of tile 0 also writes
+//                  the fresh local sums.
+// Both launches use the same block -> tile mapping, so the tile block i
+// re-reads in pass 2 was read by block i, on the same XCD, in pass 1.
+//
+// A single pass that keeps each tile in registers while the blocks exchange
+// partials through device-scope atomics was measured slower on MI355X than
+// these two launches: the cross-XCD exchange (coherent stores, arrival
+// counter, uncached reads of every partial by every block) costs more than
+// re-reading x from the cache hierarchy.
+//
 // Every thread owns one 16-byte channel vector of a token, so loads and stores
 // are 16 B wide and consecutive threads touch consecutive bytes.
+#include <algorithm>
+
 #include "dp_internal.h"
 
 namespace {
@@ -30,39 +39,23 @@ constexpr int kUnroll = 8;          // 16-byte loads in flight per thread
 struct GnArgs {
   const void* x;
   void* y;
-  float2* partial;      // [B][tiles][G]
-  const float* stale;   // [n_patches][B][G][2]
+  float2* partial;     // [B][tiles][G]
+  const float* stale;  // [n_patches][B][G][2]
   const float* gamma;
   const float* beta;
-  float* fresh;         // [B][G][2] or NULL
+  float* fresh;        // [B][G][2] or NULL
   int T, C, G, tiles, tile_tokens, n_patches, rank, B, silu;
   float inv_count, eps;
 };
 
-// Upper bound of tiles per batch item, independent of C and dtype (it sizes
-// the workspace).
+// Upper bound of tiles per batch item, independent of C, dtype and device (it
+// sizes the workspace).
 int64_t max_tiles(int64_t B, int64_t T) {
   const int64_t want = (kTargetBlocks + B - 1) / B;
   return want < T ? want : T;
 }
 
-struct GnPlan {
-  int tpp, tile_tokens, tiles;
-};
-
-GnPlan make_plan(int64_t B, int64_t T, int64_t C, dp_dtype dt) {
-  const int vec = dt == DP_BF16 ? 8 : 4;
-  const int vpt = static_cast<int>(C / vec);
-  GnPlan p;
-  p.tpp = kThreads / vpt;
-  const int64_t t0 = max_tiles(B, T);
-  int64_t tt = (T + t0 - 1) / t0;
-  tt = (tt + p.tpp - 1) / p.tpp * p.tpp;  // whole passes of the block
-  p.tile_tokens = static_cast<int>(tt);
-  p.tiles = static_cast<int>((T + tt - 1) / tt);  // <= t0
-  return p;
-}
-
+// ------------------------------------------------------------ device helpers
 template <bool BF16>
 __device__ __forceinline__ void unpack_vec(const u32x4& u, float* v) {
   if constexpr (BF16) {
@@ -96,96 +89,96 @@ __device__ __forceinline__ int64_t vec_byte(int b, int t, int vi, const GnArgs& 
   return ((static_cast<int64_t>(b) * a.T + t) * a.C) * (BF16 ? 2 : 4) + static_cast<int64_t>(vi) * 16;
 }
 
+// The 16-byte vector vi of token t, or zeros when `on` is false or t >= t_end.
 template <bool BF16>
-__global__ void __launch_bounds__(kThreads) gn_partial(GnArgs a) {
-  constexpr int VEC = BF16 ? 8 : 4;
-  __shared__ float r[2][kThreads * VEC];  // [tpp][C] per statistic
-  __shared__ float csum[2][2048];
-  const int vpt = a.C / VEC, tpp = kThreads / vpt;
-  const int tid = threadIdx.x, tl = tid / vpt, vi = tid % vpt;
-  const bool active = tl < tpp;
-  const int b = blockIdx.y, tile = blockIdx.x;
-  const int t_begin = tile * a.tile_tokens;
-  const int t_end = min(a.T, t_begin + a.tile_tokens);
-  const int npass = a.tile_tokens / tpp;
-  const char* xb = static_cast<const char*>(a.x);
-
-  float s1[VEC], s2[VEC];
-#pragma unroll
-  for (int j = 0; j < VEC; ++j) s1[j] = s2[j] = 0.f;
-  for (int k0 = 0; k0 < npass; k0 += kUnroll) {
-    u32x4 raw[kUnroll];
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int t = t_begin + tl + (k0 + u) * tpp;
-      raw[u] = u32x4{0u, 0u, 0u, 0u};
-      if (active && k0 + u < npass && t < t_end)
-        raw[u] = *reinterpret_cast<const u32x4*>(xb + vec_byte<BF16>(b, t, vi, a));
-    }
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      float v[VEC];
-      unpack_vec<BF16>(raw[u], v);
-#pragma unroll
-      for (int j = 0; j < VEC; ++j) {
-        s1[j] += v[j];
-        s2[j] = fmaf(v[j], v[j], s2[j]);
-      }
-    }
-  }
-  if (active) {
-#pragma unroll
-    for (int j = 0; j < VEC; ++j) {
-      r[0][tl * a.C + vi * VEC + j] = s1[j];
-      r[1][tl * a.C + vi * VEC + j] = s2[j];
-    }
-  }
-  __syncthreads();
-  for (int c = tid; c < a.C; c += kThreads) {  // per channel, token lanes in order
-    float p1 = 0.f, p2 = 0.f;
-    for (int k = 0; k < tpp; ++k) {
-      p1 += r[0][k * a.C + c];
-      p2 += r[1][k * a.C + c];
-    }
-    csum[0][c] = p1;
-    csum[1][c] = p2;
-  }
-  __syncthreads();
-  const int Cg = a.C / a.G;
-  for (int g = tid; g < a.G; g += kThreads) {  // per group, channels in order
-    float p1 = 0.f, p2 = 0.f;
-    for (int c = g * Cg; c < (g + 1) * Cg; ++c) {
-      p1 += csum[0][c];
-      p2 += csum[1][c];
-    }
-    a.partial[(static_cast<int64_t>(b) * a.tiles + tile) * a.G + g] = make_float2(p1, p2);
-  }
+__device__ __forceinline__ u32x4 load_or_zero(const GnArgs& a, int b, int t, int t_end, int vi, bool on) {
+  u32x4 u = u32x4{0u, 0u, 0u, 0u};
+  if (on && t < t_end)
+    u = *reinterpret_cast<const u32x4*>(static_cast<const char*>(a.x) + vec_byte<BF16>(b, t, vi, a));
+  return u;
 }
 
 template <bool BF16>
-__global__ void __launch_bounds__(kThreads) gn_apply(GnArgs a) {
+__device__ __forceinline__ void acc_vec(const u32x4& u, float* s1, float* s2) {
   constexpr int VEC = BF16 ? 8 : 4;
-  __shared__ float2 red[2048];      // [lanes][G], lanes * G <= max(G, kThreads)
-  __shared__ float2 gstat[2048];    // (mean, rstd) per group
-  const int tid = threadIdx.x;
-  const int b = blockIdx.y, tile = blockIdx.x;
-  const int G = a.G;
+  float v[VEC];
+  unpack_vec<BF16>(u, v);
+#pragma unroll
+  for (int j = 0; j < VEC; ++j) {
+    s1[j] += v[j];
+    s2[j] = fmaf(v[j], v[j], s2[j]);
+  }
+}
 
-  // ---- fold the partials of batch item b: lane q sums tiles q, q+lanes, ...
-  const int lanes = G >= kThreads ? 1 : kThreads / G;
-  const float2* pb = a.partial + static_cast<int64_t>(b) * a.tiles * G;
-  for (int f = tid; f < lanes * G; f += kThreads) {
-    const int g = f % G, q = f / G;
-    float2 s = make_float2(0.f, 0.f);
-    for (int t = q; t < a.tiles; t += lanes) {
-      const float2 p = pb[static_cast<int64_t>(t) * G + g];
-      s.x += p.x;
-      s.y += p.y;
+// gamma/beta of the thread's VEC channels (1 and 0 when NULL); vector loads
+// when the arrays are 16-byte aligned.
+__device__ __forceinline__ void load_param(const float* p, int c0, int n, float dflt, float* out) {
+  if (!p) {
+    for (int j = 0; j < n; ++j) out[j] = dflt;
+  } else if ((reinterpret_cast<uintptr_t>(p) & 15) == 0) {
+    for (int j = 0; j < n; j += 4) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(p + c0 + j);
+      out[j] = v[0];
+      out[j + 1] = v[1];
+      out[j + 2] = v[2];
+      out[j + 3] = v[3];
     }
-    red[f] = s;
+  } else {
+    for (int j = 0; j < n; ++j) out[j] = p[c0 + j];
+  }
+}
+
+template <int VEC>
+__device__ __forceinline__ void load_affine(const GnArgs& a, int vi, float* gm, float* bt) {
+  load_param(a.gamma, vi * VEC, VEC, 1.f, gm);
+  load_param(a.beta, vi * VEC, VEC, 0.f, bt);
+}
+
+// Block-wide per-group sums of the per-thread channel sums s1/s2, in a fixed
+// order: token lanes in order per channel, then channels in order per group.
+// lds_r holds [2][tpp*C] floats, lds_c [2][C]; the result lands in gsum[G].
+// Starts and ends with a barrier, so it may be called back to back.
+template <int VEC>
+__device__ void block_group_sums(const float* s1, const float* s2, bool active, int tl, int vi,
+                                 int tpp, int C, int G, float* lds_r, float* lds_c, float2* gsum) {
+  __syncthreads();
+  if (active) {
+#pragma unroll
+    for (int j = 0; j < VEC; ++j) {
+      lds_r[tl * C + vi * VEC + j] = s1[j];
+      lds_r[tpp * C + tl * C + vi * VEC + j] = s2[j];
+    }
   }
   __syncthreads();
-  for (int g = tid; g < G; g += kThreads) {
+  for (int c = threadIdx.x; c < C; c += kThreads) {
+    float p1 = 0.f, p2 = 0.f;
+    for (int k = 0; k < tpp; ++k) {
+      p1 += lds_r[k * C + c];
+      p2 += lds_r[tpp * C + k * C + c];
+    }
+    lds_c[c] = p1;
+    lds_c[C + c] = p2;
+  }
+  __syncthreads();
+  const int Cg = C / G;
+  for (int g = threadIdx.x; g < G; g += kThreads) {
+    float p1 = 0.f, p2 = 0.f;
+    for (int c = g * Cg; c < (g + 1) * Cg; ++c) {
+      p1 += lds_c[c];
+      p2 += lds_c[C + c];
+    }
+    gsum[g] = make_float2(p1, p2);
+  }
+  __syncthreads();
+}
+
+// Statistics of batch item b from the lane sums red[q*G + g] (lanes in
+// order): fresh local sums out (tile 0 only), stale sums of the other
+// patches added, (mean, rstd) per group into gstat.
+__device__ void finalize_stats(const GnArgs& a, int b, int tile, int lanes, const float2* red,
+                               float2* gstat) {
+  const int G = a.G;
+  for (int g = threadIdx.x; g < G; g += kThreads) {
     float f1 = 0.f, f2 = 0.f;
     for (int q = 0; q < lanes; ++q) {
       f1 += red[q * G + g].x;
@@ -205,53 +198,138 @@ __global__ void __launch_bounds__(kThreads) gn_apply(GnArgs a) {
     const float var = fmaxf(f2 * a.inv_count - mean * mean, 0.f);
     gstat[g] = make_float2(mean, 1.0f / sqrtf(var + a.eps));
   }
-  __syncthreads();
+}
 
-  // ---- normalise the tile
-  const int vpt = a.C / VEC, tpp = kThreads / vpt;
-  const int tl = tid / vpt, vi = tid % vpt;
-  if (tl >= tpp) return;
-  const int Cg = a.C / G;
-  float ca[VEC], cb[VEC];
+template <int VEC>
+__device__ __forceinline__ void channel_coeffs(const float2* gstat, int vi, int Cg, const float* gm,
+                                               const float* bt, float* ca, float* cb) {
 #pragma unroll
   for (int j = 0; j < VEC; ++j) {
-    const int c = vi * VEC + j;
-    const float2 ms = gstat[c / Cg];
-    const float gm = a.gamma ? a.gamma[c] : 1.f;
-    const float bt = a.beta ? a.beta[c] : 0.f;
-    ca[j] = ms.y * gm;
-    cb[j] = bt - ms.x * ca[j];
+    const float2 ms = gstat[(vi * VEC + j) / Cg];
+    ca[j] = ms.y * gm[j];
+    cb[j] = bt[j] - ms.x * ca[j];
   }
+}
+
+template <bool BF16>
+__device__ __forceinline__ void normalize_store(const GnArgs& a, int b, int t, int vi, const u32x4& u,
+                                                const float* ca, const float* cb) {
+  constexpr int VEC = BF16 ? 8 : 4;
+  float v[VEC];
+  unpack_vec<BF16>(u, v);
+#pragma unroll
+  for (int j = 0; j < VEC; ++j) {
+    float z = fmaf(v[j], ca[j], cb[j]);
+    if (a.silu) z *= __builtin_amdgcn_rcpf(1.0f + __expf(-z));  // v_rcp_f32, 1 ulp
+    v[j] = z;
+  }
+  __builtin_nontemporal_store(
+      pack_vec<BF16>(v), reinterpret_cast<u32x4*>(static_cast<char*>(a.y) + vec_byte<BF16>(b, t, vi, a)));
+}
+
+// ------------------------------------------------------------ kernels
+template <bool BF16>
+__global__ void __launch_bounds__(kThreads) gn_partial(GnArgs a) {
+  constexpr int VEC = BF16 ? 8 : 4;
+  __shared__ float lds_r[2 * kThreads * VEC];
+  __shared__ float lds_c[2 * 2048];
+  __shared__ float2 gsum[2048];
+  const int vpt = a.C / VEC, tpp = kThreads / vpt;
+  const int tid = threadIdx.x, tl = tid / vpt, vi = tid % vpt;
+  const bool active = tl < tpp;
+  const int b = blockIdx.y, tile = blockIdx.x;
   const int t_begin = tile * a.tile_tokens;
   const int t_end = min(a.T, t_begin + a.tile_tokens);
   const int npass = a.tile_tokens / tpp;
-  const char* xb = static_cast<const char*>(a.x);
-  char* yb = static_cast<char*>(a.y);
+
+  float s1[VEC], s2[VEC];
+#pragma unroll
+  for (int j = 0; j < VEC; ++j) s1[j] = s2[j] = 0.f;
   for (int k0 = 0; k0 < npass; k0 += kUnroll) {
     u32x4 raw[kUnroll];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int t = t_begin + tl + (k0 + u) * tpp;
-      if (k0 + u < npass && t < t_end)
-        raw[u] = *reinterpret_cast<const u32x4*>(xb + vec_byte<BF16>(b, t, vi, a));
+    for (int u = 0; u < kUnroll; ++u)
+      raw[u] = load_or_zero<BF16>(a, b, t_begin + tl + (k0 + u) * tpp, t_end, vi,
+                                  active && k0 + u < npass);
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u)
+      if (k0 + u < npass) acc_vec<BF16>(raw[u], s1, s2);
+  }
+  block_group_sums<VEC>(s1, s2, active, tl, vi, tpp, a.C, a.G, lds_r, lds_c, gsum);
+  for (int g = tid; g < a.G; g += kThreads)
+    a.partial[(static_cast<int64_t>(b) * a.tiles + tile) * a.G + g] = gsum[g];
+}
+
+template <bool BF16>
+__global__ void __launch_bounds__(kThreads) gn_apply(GnArgs a) {
+  constexpr int VEC = BF16 ? 8 : 4;
+  __shared__ float2 red[2048];    // [lanes][G], lanes * G <= max(G, kThreads)
+  __shared__ float2 gstat[2048];  // (mean, rstd) per group
+  const int G = a.G;
+  const int vpt = a.C / VEC, tpp = kThreads / vpt;
+  const int tid = threadIdx.x, tl = tid / vpt, vi = tid % vpt;
+  const bool active = tl < tpp;
+  const int b = blockIdx.y, tile = blockIdx.x;
+  const int t_begin = tile * a.tile_tokens;
+  const int t_end = min(a.T, t_begin + a.tile_tokens);
+  const int npass = a.tile_tokens / tpp;
+
+  // gamma/beta and the first loads of the tile go out before the fold, which
+  // then runs under their latency
+  float gm[VEC], bt[VEC];
+  if (active) load_affine<VEC>(a, vi, gm, bt);
+  u32x4 first[kUnroll];
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u)
+    first[u] = load_or_zero<BF16>(a, b, t_begin + tl + u * tpp, t_end, vi, active && u < npass);
+
+  const int lanes = G >= kThreads ? 1 : kThreads / G;
+  const float2* pb = a.partial + static_cast<int64_t>(b) * a.tiles * G;
+  for (int f = tid; f < lanes * G; f += kThreads) {
+    const int g = f % G, q = f / G;
+    float2 s = make_float2(0.f, 0.f);
+    for (int t = q; t < a.tiles; t += lanes) {
+      const float2 p = pb[static_cast<int64_t>(t) * G + g];
+      s.x += p.x;
+      s.y += p.y;
     }
+    red[f] = s;
+  }
+  __syncthreads();
+  finalize_stats(a, b, tile, lanes, red, gstat);
+  __syncthreads();
+
+  if (!active) return;
+  float ca[VEC], cb[VEC];
+  channel_coeffs<VEC>(gstat, vi, a.C / G, gm, bt, ca, cb);
+  for (int k0 = 0; k0 < npass; k0 += kUnroll) {
+    u32x4 raw[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u)
+      raw[u] = k0 == 0 ? first[u]
+                       : load_or_zero<BF16>(a, b, t_begin + tl + (k0 + u) * tpp, t_end, vi, k0 + u < npass);
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const int t = t_begin + tl + (k0 + u) * tpp;
-      if (k0 + u < npass && t < t_end) {
-        float v[VEC];
-        unpack_vec<BF16>(raw[u], v);
-#pragma unroll
-        for (int j = 0; j < VEC; ++j) {
-          float z = fmaf(v[j], ca[j], cb[j]);
-          if (a.silu) z = z / (1.0f + __expf(-z));
-          v[j] = z;
-        }
-        __builtin_nontemporal_store(pack_vec<BF16>(v),
-                                    reinterpret_cast<u32x4*>(yb + vec_byte<BF16>(b, t, vi, a)));
-      }
+      if (k0 + u < npass && t < t_end) normalize_store<BF16>(a, b, t, vi, raw[u], ca, cb);
     }
   }
+}
+
+// ------------------------------------------------------------ planning
+struct GnPlan {
+  int tile_tokens, tiles;
+};
+
+// Tokens per tile: a whole number of block passes (tpp tokens each); at most
+// max_tiles(B, T) tiles per batch item.
+GnPlan make_plan(int64_t B, int64_t T, int64_t C, dp_dtype dt) {
+  const int vec = dt == DP_BF16 ? 8 : 4;
+  const int tpp = kThreads / static_cast<int>(C / vec);
+  const int64_t per_b = max_tiles(B, T);
+  int64_t tt = (T + per_b - 1) / per_b;
+  tt = (tt + tpp - 1) / tpp * tpp;
+  return GnPlan{static_cast<int>(tt), static_cast<int>((T + tt - 1) / tt)};
 }
 
 // Workspace: the per-tile partials [B][max_tiles][G] of float2.
@@ -294,7 +372,7 @@ DP_API dp_status dp_groupnorm_stale_stats(const void* x, const float* stale_sums
     return fail(DP_ERR_INVALID_ARG, "dp_groupnorm_stale_stats: workspace %zu < %zu bytes",
                 ws_bytes, need);
   const int vec = dt == DP_BF16 ? 8 : 4;
-  if (C % vec != 0 || C > 2048 || C / vec > kThreads || T_loc > 0x7FFFFFFF || B > 65535 || G > 65535 ||
+  if (C % vec != 0 || C > 2048 || C / vec > kThreads || T_loc > 0x7FFFFFFF || B > 65535 ||
       B * G > 0x7FFFFFFF)
     return fail(DP_ERR_UNSUPPORTED, "dp_groupnorm_stale_stats: C=%lld G=%lld not supported",
                 (long long)C, (long long)G);
@@ -302,8 +380,8 @@ DP_API dp_status dp_groupnorm_stale_stats(const void* x, const float* stale_sums
   const size_t xb = static_cast<size_t>(B * T_loc * C) * es;
   if (dp::overlaps(x, xb, y, xb)) return fail(DP_ERR_INVALID_ARG, "dp_groupnorm_stale_stats: x and y overlap");
 
-  GnArgs ga;
   const GnPlan p = make_plan(B, T_loc, C, dt);
+  GnArgs ga;
   ga.x = x;
   ga.y = y;
   ga.partial = static_cast<float2*>(ws);
@@ -323,6 +401,7 @@ DP_API dp_status dp_groupnorm_stale_stats(const void* x, const float* stale_sums
   ga.inv_count = static_cast<float>(1.0 / (static_cast<double>(T_total) * (C / G)));
   ga.eps = eps;
   const dim3 grid(static_cast<unsigned>(p.tiles), static_cast<unsigned>(B));
+  dp::clear_error();
   if (dt == DP_BF16) {
     hipLaunchKernelGGL(gn_partial<true>, grid, dim3(kThreads), 0, stream, ga);
     hipLaunchKernelGGL(gn_apply<true>, grid, dim3(kThreads), 0, stream, ga);

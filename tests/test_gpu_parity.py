@@ -98,6 +98,7 @@ def stale_sums_for(B, T_rem, C, G, N, seed, dt):
     ("bf16", 2, 1024, 640, 32, 4, 1, False, True), ("bf16", 2, 300, 320, 32, 2, 1, True, True),
     ("bf16", 1, 17, 64, 8, 1, 0, False, False), ("f32", 2, 512, 64, 32, 2, 0, False, True),
     ("f32", 2, 100, 12, 4, 3, 2, True, False), ("bf16", 2, 64, 1280, 32, 2, 0, True, True),
+    ("bf16", 1, 40, 1024, 1024, 2, 1, False, True),  # one channel per group
 ])
 def test_groupnorm(dt, B, T, C, G, N, rank, silu, affine):
     say("gn", dt, B, T, C, G, N, rank, silu, affine)
