@@ -11,18 +11,24 @@
 // -------------------------------
 // A block of 4 waves owns 128 consecutive queries of one (batch, head); each
 // wave owns 32 of them.  Key/value tiles of 64 tokens are staged in LDS
-// (K as [key][d], V transposed as [d][key]), double-buffered with one barrier
-// per tile.  Per 32-key block a wave computes the transposed scores
+// (K as [key][d], V as [key][d] read transposed) by LDS DMA in a 3-stage
+// ring, the next tile's load in flight during the current one, one barrier
+// per tile; 48 KB per block lets three blocks share a CU.  Per 32-key
+// block a wave computes the transposed scores
 //     S^T[key][query] = K . Q^T      (v_mfma_f32_32x32x16_bf16, 4 k-steps over d)
 // so that accumulator lane l holds 16 scores of the single query l % 32: the
-// softmax max/sum are in-lane, plus one exchange with lane l ^ 32.  K rows are
-// loaded with row index bits 2 and 3 swapped; with that permutation the 8
+// softmax is in-lane, plus one exchange with lane l ^ 32.  K rows are loaded
+// with row index bits 2 and 3 swapped; with that permutation the 8
 // probabilities a lane holds for each 16-key step are 8 consecutive keys, which
 // is exactly the B operand layout of the transposed output product
 //     O^T[d][query] += V^T . P^T      (2 d-blocks x 2 k-steps per 32 keys).
-// Online softmax in base 2 (scale * log2 e folded into one FMA per score),
-// float32 running max and per-lane partial row sums, P rounded to bf16 for
-// the second product.  Output rows are normalised once at the end.
+// Softmax in base 2: a probability is exp2(c * s - m_ref) with c = scale *
+// log2(e) applied to the float32 score s by one FMA (Q enters the product as
+// stored, so no rounding of q * c to bf16 perturbs the scores).  The reference
+// m_ref is the first block's max and only moves when a block's probabilities
+// would grow huge (see the key loop).  P is rounded to bf16 for the second
+// product; row sums and O accumulate in float32; output rows are normalised
+// once at the end.
 //
 // f32 (d = 32 or 64)
 // ------------------
@@ -40,10 +46,10 @@ namespace {
 constexpr int kD = 64;
 constexpr int kBMq = 128;              // queries per block (4 waves x 32)
 constexpr int kBNk = 64;               // keys per tile
-constexpr int kStages = 3;             // LDS ring depth (loads run two tiles ahead)
+constexpr int kStages = 3;             // LDS ring depth (the next tile loads during the current one)
 constexpr int kTileBytes = kBNk * kD * 2;
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kRescale = 8.0f;       // lazy rescale: probabilities may reach 2^8
+constexpr float kBig = 1.8446744e19f;  // 2^64: a lane's block sum above this recentres
 constexpr int kXcds = 8;
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -105,24 +111,12 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rsrc, int voff, uns
 }
 #pragma clang diagnostic pop
 
-// acc + lo + hi of a packed bf16 pair, in float32 (v_dot2_f32_bf16 against
-// (1, 1)), so the row sums use exactly the rounded probabilities of the P.V
-// product.  The VOP3P form is written out: the accumulate-in-place VOP2 form
-// (v_dot2c_f32_bf16) read wrong values on gfx950 right after the
-// v_cvt_pk_bf16_f32 that produced its operand, and the builtin lowers to it.
-__device__ __forceinline__ float sum_bf16_pair(float acc, unsigned int pair) {
-  const unsigned int ones = 0x3F803F80u;
-  float r;
-  asm("v_dot2_f32_bf16 %0, %1, %2, %3" : "=v"(r) : "v"(pair), "v"(ones), "v"(acc));
-  return r;
-}
-
 template <int S>
 struct Stage {
   static constexpr int value = S;
 };
 
-__global__ void __launch_bounds__(256, 2) attn_bf16_d64(AttnArgs a) {
+__global__ void __launch_bounds__(256, 3) attn_bf16_d64(AttnArgs a) {
   // K tiles at stage*8 KB, V tiles at 24 KB + stage*8 KB.
   __shared__ __attribute__((aligned(1024))) char lds[kStages * 2 * kTileBytes];
   constexpr int kVring = kStages * kTileBytes;
@@ -148,18 +142,14 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_d64(AttnArgs a) {
   const int qi = qb * kBMq + wave * 32 + l32;
   const bool q_ok = qi < a.Tq;
 
-  // Q, pre-multiplied by scale*log2(e) in float32 and rounded once to bf16,
-  // so that an accumulator started at -m_ref holds the exponent directly.
+  // Q as stored (the scale is applied to the float32 scores).
   bf16x8 qop[4];
   {
     const bf16_t* qp = a.q + (static_cast<int64_t>(b) * a.Tq + (q_ok ? qi : 0)) * C + h * kD + 8 * g;
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
       const u32x4 w = q_ok ? *reinterpret_cast<const u32x4*>(qp + 16 * st) : u32x4{0u, 0u, 0u, 0u};
-      u32x4 sw;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) sw[j] = pack_bf16x2(bf16_lo(w[j]) * a.c, bf16_hi(w[j]) * a.c);
-      qop[st] = __builtin_bit_cast(bf16x8, sw);
+      qop[st] = __builtin_bit_cast(bf16x8, w);
     }
     // Consume Q here so its loads are complete before the key loop; otherwise
     // the compiler would keep a vmcnt(0) wait for them in every iteration,
@@ -220,104 +210,164 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_d64(AttnArgs a) {
     }
   };
 
-  float m_ref = 0.f, l_part = 0.f;  // m_ref: base-2 reference the scores are shifted by
-  f32x16 o[2], bias;
+  // Software pipeline over 32-key blocks j (two per 64-key tile).  Slot j
+  // issues the scores of block j+1 and the P.V product of block j-1 (8 MFMAs)
+  // and, independent of both, the exponentials, bf16 probabilities and row
+  // sums of block j, so the MFMA and VALU pipes can run side by side.
+  //
+  // Reference: a block's probabilities are exp2(c * s - m_ref), c = scale *
+  // log2(e), s the raw float32 scores.  m_ref is set once from the first
+  // block's max; later blocks only need a new reference when their
+  // probabilities grow huge, which the lane's block row sum reveals (it also
+  // catches inf).  That rare case is handled at the slot boundary: move the
+  // reference to the block max, rescale o and l, and recompute the block's
+  // probabilities.
+  const float cs = a.c;
+  float m_ref = 0.f, l_part = 0.f;
+  f32x16 o[2], sc_cur, sc_nxt;
+  bf16x8 p_prv[2];
 #pragma unroll
-  for (int e = 0; e < 16; ++e) o[0][e] = o[1][e] = bias[e] = 0.f;
+  for (int e = 0; e < 16; ++e) o[0][e] = o[1][e] = 0.f;
 
-  // One tile: scores, softmax and P.V from LDS stage S; tile t+2 is issued
-  // into stage (S+2)%3 first.
-  auto step = [&](auto stage_c, int t) {
-    constexpr int S = decltype(stage_c)::value;
-    if (t + 1 < t_end) {
-      asm volatile("s_waitcnt vmcnt(4)" ::: "memory");  // tile t done, t+1 may be in flight
-    } else {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    }
-    __syncthreads();  // tile t visible; stage of tile t-1 no longer read
-    if (t + 2 < t_end) issue(t + 2, (S + 2) % 3);
-
-    f32x16 sc[2];
+  auto qk = [&](auto ks_c, auto kb_c) {
+    constexpr int KS = decltype(ks_c)::value, KB = decltype(kb_c)::value;
+    bf16x8 ka[4];
 #pragma unroll
-    for (int blk = 0; blk < 2; ++blk)
+    for (int st = 0; st < 4; ++st)
+      ka[st] = *reinterpret_cast<const bf16x8*>(lds + KS * kTileBytes + KB * 4096 + koff[st]);
+    f32x16 r = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[0], qop[0], f32x16{}, 0, 0, 0);
 #pragma unroll
-      for (int st = 0; st < 4; ++st) {
-        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(lds + S * kTileBytes + blk * 4096 + koff[st]);
-        sc[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qop[st], st == 0 ? bias : sc[blk], 0, 0, 0);
-      }
-    if ((t + 1) * kBNk > a.Tkv) {  // ragged last tile
-#pragma unroll
-      for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int r = 8 * (e >> 2) + 4 * g + (e & 3);
-          const int pr = (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
-          if (t * kBNk + 32 * blk + pr >= a.Tkv) sc[blk][e] = -INFINITY;
-        }
-    }
-    float mx = fmaxf(sc[0][0], sc[1][0]);
-#pragma unroll
-    for (int e = 1; e < 16; ++e) mx = fmaxf(fmaxf(mx, sc[0][e]), sc[1][e]);  // v_max3 chain
-    const float mt = swap_max(mx);  // tile max relative to m_ref
-    if (t == t_begin || __builtin_amdgcn_ballot_w64(mt > kRescale)) {
-      // Move the reference: on the first tile to the tile max (o and l are
-      // still zero), later only when a score would exceed 2^kRescale.
-      const float delta = t == t_begin ? mt : fmaxf(mt, 0.f);
-      if (t != t_begin) {
-        const float alpha = __builtin_amdgcn_exp2f(-delta);
-        l_part *= alpha;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          o[0][e] *= alpha;
-          o[1][e] *= alpha;
-        }
-      }
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        sc[0][e] -= delta;
-        sc[1][e] -= delta;
-      }
-      m_ref += delta;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) bias[e] = -m_ref;
-    }
-    bf16x8 pb[2][2];
-    float ls0 = 0.f, ls1 = 0.f;
-#pragma unroll
-    for (int blk = 0; blk < 2; ++blk) {
-#pragma unroll
-      for (int e = 0; e < 16; ++e) sc[blk][e] = __builtin_amdgcn_exp2f(sc[blk][e]);
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        pb[blk][s2] = pack8(sc[blk], 8 * s2);
-        const u32x4 w = __builtin_bit_cast(u32x4, pb[blk][s2]);
-        ls0 = sum_bf16_pair(ls0, w[0]);
-        ls1 = sum_bf16_pair(ls1, w[1]);
-        ls0 = sum_bf16_pair(ls0, w[2]);
-        ls1 = sum_bf16_pair(ls1, w[3]);
-      }
-    }
-    l_part += ls0 + ls1;
+    for (int st = 1; st < 4; ++st) r = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[st], qop[st], r, 0, 0, 0);
+    return r;
+  };
+  auto pv = [&](auto vs_c, auto vb_c) {
+    constexpr int VS = decltype(vs_c)::value, VB = decltype(vb_c)::value;
 #pragma unroll
     for (int db = 0; db < 2; ++db)
 #pragma unroll
-      for (int blk = 0; blk < 2; ++blk)
+      for (int s2 = 0; s2 < 2; ++s2) {
+        const char* vb = lds + VS * kTileBytes + VB * 4096 + s2 * 2048;
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vb + voff[db][0]));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vb + voff[db][1]));
+        const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, p_prv[s2], o[db], 0, 0, 0);
+      }
+  };
+  // keys of block (t, blk) at or beyond T_kv get -inf (only the last tile)
+  auto mask = [&](f32x16& x, int t, int blk) {
 #pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-          const char* vb = lds + S * kTileBytes + blk * 4096 + s2 * 2048;
-          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vb + voff[db][0]));
-          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vb + voff[db][1]));
-          const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[blk][s2], o[db], 0, 0, 0);
-        }
+    for (int e = 0; e < 16; ++e) {
+      const int r = 8 * (e >> 2) + 4 * g + (e & 3);
+      const int pr = (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
+      if (t * kBNk + 32 * blk + pr >= a.Tkv) x[e] = -INFINITY;
+    }
+  };
+  // Exponentials, bf16 probabilities and the lane's row sum of one block.  The
+  // sum adds the float32 exponentials with plain adds the compiler schedules
+  // itself; against the bf16-rounded P of the product this is an unbiased
+  // relative 2^-9 per term.  (A dot2 of the packed pairs would be fewer
+  // instructions, but DOT results need wait states that the compiler cannot
+  // see through inline assembly, and the VOP2 form read wrong values on gfx950.)
+  auto probs = [&](const f32x16& x, bf16x8* p) {
+    f32x16 ex;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) ex[e] = __builtin_amdgcn_exp2f(fmaf(x[e], cs, -m_ref));
+    p[0] = pack8(ex, 0);
+    p[1] = pack8(ex, 8);
+    float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+    for (int e = 0; e < 16; e += 2) {
+      s0 += ex[e];
+      s1 += ex[e + 1];
+    }
+    return s0 + s1;
+  };
+  // Move the reference to the block max (when above it): rescale o and l.
+  auto recentre = [&](const f32x16& x) {
+    float mx = x[0];
+#pragma unroll
+    for (int e = 1; e < 16; ++e) mx = fmaxf(mx, x[e]);
+    const float delta = fmaxf(fmaf(swap_max(mx), cs, -m_ref), 0.f);
+    const float alpha = __builtin_amdgcn_exp2f(-delta);
+    l_part *= alpha;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      o[0][e] *= alpha;
+      o[1][e] *= alpha;
+    }
+    m_ref += delta;
   };
 
+  // One slot: block (t, blk) is current; K of the next block at (KS, KB), V of
+  // the previous one at (VS, VB).  Straight-line from the MFMAs to the row
+  // sums so that the scheduler can interleave them; the ragged-key mask and
+  // the rare recentring sit at the slot boundaries.
+  auto slot = [&](auto ks_c, auto kb_c, auto vs_c, auto vb_c, bool ragged, int t, int blk) {
+    if (ragged) mask(sc_cur, t, blk);
+    sc_nxt = qk(ks_c, kb_c);
+    pv(vs_c, vb_c);
+    bf16x8 p_new[2];
+    float ls = probs(sc_cur, p_new);
+    if (__builtin_amdgcn_ballot_w64(!(ls < kBig))) {  // rare
+      recentre(sc_cur);
+      ls = probs(sc_cur, p_new);
+    }
+    l_part += ls;
+    p_prv[0] = p_new[0];
+    p_prv[1] = p_new[1];
+    sc_cur = sc_nxt;
+  };
+  // Tile t in LDS stage S: slot (t, 0), then wait for tile t+1 and refill the
+  // stage of tile t-1 with tile t+3, then slot (t, 1).  The first tile's slot
+  // (t, 0) multiplies a zero P by a zeroed V stage; the last tile's slot (t, 1)
+  // computes scores of a block that does not exist and never uses them.
+  auto tile = [&](auto stage_c, int t) {
+    constexpr int S = decltype(stage_c)::value;
+    const bool ragged = (t + 1) * kBNk > a.Tkv;
+    slot(Stage<S>{}, Stage<1>{}, Stage<(S + 2) % 3>{}, Stage<1>{}, ragged, t, 0);
+    if (t + 1 < t_end) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // tile t+1 done
+      __syncthreads();  // tile t+1 visible; stage of tile t-1 no longer read
+      if (t + 2 < t_end) issue(t + 2, (S + 2) % 3);
+    }
+    slot(Stage<(S + 1) % 3>{}, Stage<0>{}, Stage<S>{}, Stage<0>{}, ragged, t, 1);
+  };
+
+  // zero V of stage 3, read (times a zero P) by the first tile's first slot
+  {
+    u32x4* z = reinterpret_cast<u32x4*>(lds + kVring + 2 * kTileBytes);
+    z[tid] = u32x4{0u, 0u, 0u, 0u};
+    z[tid + 256] = u32x4{0u, 0u, 0u, 0u};
+  }
+  p_prv[0] = p_prv[1] = bf16x8{};
   issue(t_begin, 0);
   if (t_begin + 1 < t_end) issue(t_begin + 1, 1);
-  for (int t = t_begin; t < t_end; t += 3) {
-    step(Stage<0>{}, t);
-    if (t + 1 < t_end) step(Stage<1>{}, t + 1);
-    if (t + 2 < t_end) step(Stage<2>{}, t + 2);
+  if (t_begin + 1 < t_end) {
+    asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+  } else {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
+  __syncthreads();
+  // first block: its max is the reference
+  sc_cur = qk(Stage<0>{}, Stage<0>{});
+  if ((t_begin + 1) * kBNk > a.Tkv) mask(sc_cur, t_begin, 0);
+  {
+    float mx = sc_cur[0];
+#pragma unroll
+    for (int e = 1; e < 16; ++e) mx = fmaxf(mx, sc_cur[e]);
+    m_ref = swap_max(mx) * cs;
+  }
+  tile(Stage<0>{}, t_begin);
+  for (int t = t_begin + 1; t < t_end; t += 3) {
+    tile(Stage<1>{}, t);
+    if (t + 1 < t_end) tile(Stage<2>{}, t + 1);
+    if (t + 2 < t_end) tile(Stage<0>{}, t + 2);
+  }
+  // P.V of the last block
+  switch ((t_end - 1 - t_begin) % 3) {
+    case 0: pv(Stage<0>{}, Stage<1>{}); break;
+    case 1: pv(Stage<1>{}, Stage<1>{}); break;
+    default: pv(Stage<2>{}, Stage<1>{}); break;
   }
 
   const float l_tot = swap_sum(l_part);

@@ -145,15 +145,40 @@ def test_attention(dt, B, H, d, Tq, Tkv):
     assert_close(host(out), oracle.attention(q, k, v, H), dt, "attention")
 
 
-def test_attention_peaked_scores_bf16():
-    """Large-magnitude queries: softmax close to one-hot, exercising the
-    running-max rescale across key tiles."""
-    B, H, d, Tq, Tkv = 1, 2, 64, 130, 700
-    q = R(5, "atp.q", (B, Tq, H * d), "bf16", 3.0)
+@pytest.mark.parametrize("Tq,Tkv,qscale", [(130, 700, 3.0), (70, 3001, 4.0), (64, 6000, 2.0), (33, 129, 4.0)])
+def test_attention_peaked_scores_bf16(Tq, Tkv, qscale):
+    """Large-magnitude queries: softmax close to one-hot, so later key blocks
+    can exceed the first block's max by far and force the reference to move
+    (the 6000-key case also splits the key range across blocks)."""
+    say("attn peaked", Tq, Tkv, qscale)
+    B, H, d = 1, 2, 64
+    q = R(5, "atp.q", (B, Tq, H * d), "bf16", qscale)
     k = R(5, "atp.k", (B, Tkv, H * d), "bf16", 1.0)
     v = R(5, "atp.v", (B, Tkv, H * d), "bf16", 1.0)
     out = ops.dp_attn_stale_kv(dev(q, "bf16"), dev(k, "bf16"), dev(v, "bf16"), H)
     assert_close(host(out), oracle.attention(q, k, v, H), "bf16", "attention peaked")
+
+
+@pytest.mark.parametrize("Tq,Tkv,hot", [(64, 300, (128, 192)), (32, 9000, (8500, 8600))])
+def test_attention_reference_moves(Tq, Tkv, hot):
+    """A run of identical keys scoring ~69 (log2 units) above every earlier key:
+    the kernel must move its softmax reference mid-sequence (rescaling the
+    accumulated output, the row sums and the next block's scores already
+    issued).  All queries are equal and the hot keys share one value vector,
+    so the exact result is that vector (the other keys weigh < 2^-60).  The
+    long case also splits the key range, so the partial results carry
+    references 2^-69 apart into the combine."""
+    say("attn reference moves", Tq, Tkv, hot)
+    B, H, d = 1, 2, 64
+    q = np.full((B, Tq, H * d), 0.5)
+    k = R(6, "atm.k", (B, Tkv, H * d), "bf16", 1.0)
+    v = R(6, "atm.v", (B, Tkv, H * d), "bf16", 1.0)
+    k[:, hot[0]:hot[1]] = 12.0
+    v[:, hot[0]:hot[1]] = v[:, hot[0]]
+    ref = oracle.attention(q, k, v, H)
+    assert np.allclose(ref, np.broadcast_to(v[:, hot[0]][:, None, :], ref.shape), atol=1e-12)
+    out = ops.dp_attn_stale_kv(dev(q, "bf16"), dev(k, "bf16"), dev(v, "bf16"), H)
+    assert_close(host(out), ref, "bf16", "attention reference moves")
 
 
 # ---------------------------------------------------------------- error paths
