@@ -263,24 +263,39 @@ __global__ void __launch_bounds__(256, 3) attn_bf16_d64(AttnArgs a) {
     }
   };
   // Exponentials, bf16 probabilities and the lane's row sum of one block.  The
-  // sum adds the float32 exponentials with plain adds the compiler schedules
-  // itself; against the bf16-rounded P of the product this is an unbiased
-  // relative 2^-9 per term.  (A dot2 of the packed pairs would be fewer
-  // instructions, but DOT results need wait states that the compiler cannot
-  // see through inline assembly, and the VOP2 form read wrong values on gfx950.)
+  // sum is taken over the bf16-rounded P that enters the product, as eight
+  // v_dot2_f32_bf16 against (1, 1) in four independent chains, in one asm
+  // block: the compiler cannot see DOT hazards through inline assembly (and
+  // its own v_dot2c form read wrong values on gfx950 right after the pack), so
+  // the block carries its own wait states -- five before the first DOT, three
+  // instructions between dependent DOTs, five before plain VALU reads of DOT
+  // results.
   auto probs = [&](const f32x16& x, bf16x8* p) {
     f32x16 ex;
 #pragma unroll
     for (int e = 0; e < 16; ++e) ex[e] = __builtin_amdgcn_exp2f(fmaf(x[e], cs, -m_ref));
     p[0] = pack8(ex, 0);
     p[1] = pack8(ex, 8);
-    float s0 = 0.f, s1 = 0.f;
-#pragma unroll
-    for (int e = 0; e < 16; e += 2) {
-      s0 += ex[e];
-      s1 += ex[e + 1];
-    }
-    return s0 + s1;
+    const u32x4 w0 = __builtin_bit_cast(u32x4, p[0]), w1 = __builtin_bit_cast(u32x4, p[1]);
+    const unsigned int ones = 0x3F803F80u;
+    float r0, r1, r2, r3;
+    asm("s_nop 4\n\t"
+        "v_dot2_f32_bf16 %0, %4, %12, 0\n\t"
+        "v_dot2_f32_bf16 %1, %5, %12, 0\n\t"
+        "v_dot2_f32_bf16 %2, %6, %12, 0\n\t"
+        "v_dot2_f32_bf16 %3, %7, %12, 0\n\t"
+        "v_dot2_f32_bf16 %0, %8, %12, %0\n\t"
+        "v_dot2_f32_bf16 %1, %9, %12, %1\n\t"
+        "v_dot2_f32_bf16 %2, %10, %12, %2\n\t"
+        "v_dot2_f32_bf16 %3, %11, %12, %3\n\t"
+        "s_nop 4\n\t"
+        "v_add_f32 %0, %0, %1\n\t"
+        "v_add_f32 %2, %2, %3\n\t"
+        "v_add_f32 %0, %0, %2"
+        : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3)
+        : "v"(w0[0]), "v"(w0[1]), "v"(w0[2]), "v"(w0[3]), "v"(w1[0]), "v"(w1[1]), "v"(w1[2]), "v"(w1[3]),
+          "v"(ones));
+    return r0;
   };
   // Move the reference to the block max (when above it): rescale o and l.
   auto recentre = [&](const f32x16& x) {
