@@ -13,8 +13,9 @@
 // bf16 path (gfx950): a 256-thread block computes a 128x128, 128x64, 64x128 or
 // 64x64 output tile (chosen per problem so the tiles spread evenly over the
 // CUs); tiles sharing A rows are dealt to one XCD.  K moves through a 3-stage
-// LDS ring in 32-wide slices by direct global->LDS loads (two slices ahead),
-// 64-byte rows XOR-swizzled.  Each wave owns a quarter of the tile as
+// LDS ring by direct global->LDS loads issued two stages ahead; a stage holds
+// two 32-wide sub-slices (one when K is not a multiple of 64), so each barrier
+// covers 64 of K.  Sub-slice rows are 64 bytes, XOR-swizzled.  Each wave owns a quarter of the tile as
 // v_mfma_f32_32x32x16_bf16 blocks computed as (W rows) x (A rows)^T, so an
 // accumulator lane holds 4 consecutive output channels of one output row and
 // the epilogue writes 8-byte runs.
@@ -26,8 +27,9 @@
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kBK = 32;            // reduction slice (64 bytes of bf16 per row)
-constexpr int kStages = 3;         // LDS ring depth (loads run two slices ahead)
+constexpr int kBK = 32;            // reduction sub-slice (64 bytes of bf16 per row)
+constexpr int kSub = 2;            // sub-slices per ring stage when K allows (64 of K per barrier)
+constexpr int kStages = 3;         // LDS ring depth (loads run two stages ahead)
 constexpr int kXcds = 8;
 
 // Zero page read by padding rows of the implicit im2col (columns outside the
@@ -72,11 +74,8 @@ __device__ __forceinline__ void gdma16(const void* gsrc, unsigned int m0) {
 
 template <int N>
 __device__ __forceinline__ void wait_vm() {
-  static_assert(N == 0 || N == 2 || N == 3 || N == 4, "vmcnt");
-  if constexpr (N == 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-  else if constexpr (N == 3) asm volatile("s_waitcnt vmcnt(3)" ::: "memory");
-  else if constexpr (N == 2) asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
-  else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
 template <int S>
@@ -87,15 +86,17 @@ struct Stage {
 // One block computes a BM x BN output tile with 4 waves arranged 2 x 2; each
 // wave owns (BM/2) x (BN/2) as 32 x 32 MFMA blocks computed as (W rows) x
 // (A rows)^T, so an accumulator lane holds 4 consecutive output channels of one
-// output row.  K advances in 32-wide slices through a 3-stage LDS ring.
-template <int BM, int BN, bool CONV>
+// output row.  K advances SUB 32-wide sub-slices per stage through an ST-stage
+// LDS ring.
+template <int BM, int BN, int SUB, int ST, bool CONV>
 __global__ void __launch_bounds__(kThreads, 2) gemm_bf16(GemmArgs g) {
   constexpr int kABytes = BM * kBK * 2, kBBytes = BN * kBK * 2;
-  constexpr int kStageBytes = kABytes + kBBytes;
+  constexpr int kSubBytes = kABytes + kBBytes;         // one 32-wide sub-slice
+  constexpr int kStageBytes = SUB * kSubBytes;
   constexpr int kASlabs = BM / 64, kBSlabs = BN / 64;  // 1 KB DMA slabs per wave
-  constexpr int kDma = kASlabs + kBSlabs;              // DMA instructions per slice per wave
+  constexpr int kDma = SUB * (kASlabs + kBSlabs);      // DMA instructions per stage per wave
   constexpr int WM = BM / 2, WN = BN / 2, MB = WM / 32, NB = WN / 32;
-  __shared__ __attribute__((aligned(1024))) char lds[kStages * kStageBytes];
+  __shared__ __attribute__((aligned(1024))) char lds[ST * kStageBytes];
 
   const int u = (blockIdx.x % kXcds) * g.units_per_xcd + blockIdx.x / kXcds;
   if (u >= g.units) return;
@@ -161,29 +162,32 @@ __global__ void __launch_bounds__(kThreads, 2) gemm_bf16(GemmArgs g) {
     }
   };
 
-  const int n_kt = g.K / kBK;
-  const int kpt = CONV ? g.geo.Cin / kBK : n_kt;  // slices per conv tap
+  const int n_kt = g.K / (kBK * SUB);
+  const int kpt = CONV ? g.geo.Cin / kBK : g.K / kBK;  // 32-wide sub-slices per conv tap
   // Issues slice kt into stage st: A slabs then B slabs; pointers advance one
   // slice (64 bytes) per issue, and conv rows are re-pointed at each tap.
   int tap_next = 0, in_tap = 0;
   auto issue = [&](int st) {
-    if constexpr (CONV) {
-      if (in_tap == 0) conv_rows(tap_next);
-    }
 #pragma unroll
-    for (int j = 0; j < kASlabs; ++j) {
-      gdma16(asrc[j], lds0 + st * kStageBytes + j * 4096);
-      asrc[j] += kBK * 2;
-    }
+    for (int u = 0; u < SUB; ++u) {
+      if constexpr (CONV) {
+        if (in_tap == 0) conv_rows(tap_next);
+      }
 #pragma unroll
-    for (int j = 0; j < kBSlabs; ++j) {
-      gdma16(bsrc[j], lds0 + st * kStageBytes + kABytes + j * 4096);
-      bsrc[j] += kBK * 2;
-    }
-    if constexpr (CONV) {
-      if (++in_tap == kpt) {
-        in_tap = 0;
-        ++tap_next;
+      for (int j = 0; j < kASlabs; ++j) {
+        gdma16(asrc[j], lds0 + st * kStageBytes + u * kSubBytes + j * 4096);
+        asrc[j] += kBK * 2;
+      }
+#pragma unroll
+      for (int j = 0; j < kBSlabs; ++j) {
+        gdma16(bsrc[j], lds0 + st * kStageBytes + u * kSubBytes + kABytes + j * 4096);
+        bsrc[j] += kBK * 2;
+      }
+      if constexpr (CONV) {
+        if (++in_tap == kpt) {
+          in_tap = 0;
+          ++tap_next;
+        }
       }
     }
   };
@@ -215,31 +219,41 @@ __global__ void __launch_bounds__(kThreads, 2) gemm_bf16(GemmArgs g) {
 
   auto step = [&](auto stage_c, int kt) {
     constexpr int S = decltype(stage_c)::value;
-    if (kt + 1 < n_kt) wait_vm<kDma>();
+    if (kt + ST - 2 < n_kt) wait_vm<(ST - 2) * kDma>();  // stage kt done, later ones may be in flight
     else wait_vm<0>();
-    __syncthreads();  // slice kt visible; the stage of slice kt-1 is free
-    if (kt + 2 < n_kt) issue((S + 2) % 3);
+    __syncthreads();  // stage kt visible; the stage of kt-1 is free
+    if (kt + ST - 1 < n_kt) issue((S + ST - 1) % ST);
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      bf16x8 wa[NB], xb[MB];
+    for (int u = 0; u < SUB; ++u)
 #pragma unroll
-      for (int i = 0; i < NB; ++i) wa[i] = *reinterpret_cast<const bf16x8*>(lds + S * kStageBytes + boff[i][s]);
+      for (int s = 0; s < 2; ++s) {
+        bf16x8 wa[NB], xb[MB];
 #pragma unroll
-      for (int j = 0; j < MB; ++j) xb[j] = *reinterpret_cast<const bf16x8*>(lds + S * kStageBytes + aoff[j][s]);
-#pragma unroll
-      for (int i = 0; i < NB; ++i)
+        for (int i = 0; i < NB; ++i)
+          wa[i] = *reinterpret_cast<const bf16x8*>(lds + S * kStageBytes + u * kSubBytes + boff[i][s]);
 #pragma unroll
         for (int j = 0; j < MB; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wa[i], xb[j], acc[i][j], 0, 0, 0);
-    }
+          xb[j] = *reinterpret_cast<const bf16x8*>(lds + S * kStageBytes + u * kSubBytes + aoff[j][s]);
+#pragma unroll
+        for (int i = 0; i < NB; ++i)
+#pragma unroll
+          for (int j = 0; j < MB; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wa[i], xb[j], acc[i][j], 0, 0, 0);
+      }
   };
 
-  issue(0);
-  if (n_kt > 1) issue(1);
-  for (int kt = 0; kt < n_kt; kt += 3) {
+#pragma unroll
+  for (int p = 0; p < ST - 1; ++p)
+    if (p < n_kt) issue(p);
+  for (int kt = 0; kt < n_kt; kt += ST) {
     step(Stage<0>{}, kt);
     if (kt + 1 < n_kt) step(Stage<1>{}, kt + 1);
-    if (kt + 2 < n_kt) step(Stage<2>{}, kt + 2);
+    if constexpr (ST > 2) {
+      if (kt + 2 < n_kt) step(Stage<2 % ST>{}, kt + 2);
+    }
+    if constexpr (ST > 3) {
+      if (kt + 3 < n_kt) step(Stage<3 % ST>{}, kt + 3);
+    }
   }
 
   // Epilogue: lane holds rows n = 8*(e/4) + 4*gq + e%4 of column m = l32.
@@ -287,8 +301,14 @@ void launch_bf16(const GemmArgs& base, hipStream_t st) {
   g.tiles_n = (g.N + BN - 1) / BN;
   g.units = g.tiles_m * g.tiles_n;
   g.units_per_xcd = (g.units + kXcds - 1) / kXcds;
-  hipLaunchKernelGGL((gemm_bf16<BM, BN, CONV>), dim3(static_cast<unsigned>(g.units_per_xcd * kXcds)),
-                     dim3(kThreads), 0, st, g);
+  const dim3 grid(static_cast<unsigned>(g.units_per_xcd * kXcds));
+  // two sub-slices per stage when K allows, except for the 128x128 tile, whose
+  // 96 KB ring would leave room for one block per CU
+  constexpr int SUB = BM * BN >= 128 * 128 ? 1 : kSub;
+  if (SUB > 1 && g.K % (SUB * kBK) == 0)
+    hipLaunchKernelGGL((gemm_bf16<BM, BN, SUB, kStages, CONV>), grid, dim3(kThreads), 0, st, g);
+  else
+    hipLaunchKernelGGL((gemm_bf16<BM, BN, 1, kStages, CONV>), grid, dim3(kThreads), 0, st, g);
 }
 
 // Tile shape: fewest tile-rounds per CU, weighting smaller tiles by their
