@@ -13,9 +13,10 @@
 // bf16 path (gfx950): a 256-thread block computes a 128x128, 128x64, 64x128 or
 // 64x64 output tile (chosen per problem so the tiles spread evenly over the
 // CUs); tiles sharing A rows are dealt to one XCD.  K moves through a 3-stage
-// LDS ring by direct global->LDS loads issued two stages ahead; a stage holds
-// two 32-wide sub-slices (one when K is not a multiple of 64), so each barrier
-// covers 64 of K.  Sub-slice rows are 64 bytes, XOR-swizzled.  Each wave owns a quarter of the tile as
+// LDS ring (2 stages for the 128x128 tile) by direct global->LDS loads issued
+// ahead; a stage holds two 32-wide sub-slices (one when K is not a multiple of
+// 64), so each barrier covers 64 of K.  Sub-slice rows are 64 bytes,
+// XOR-swizzled.  Each wave owns a quarter of the tile as
 // v_mfma_f32_32x32x16_bf16 blocks computed as (W rows) x (A rows)^T, so an
 // accumulator lane holds 4 consecutive output channels of one output row and
 // the epilogue writes 8-byte runs.
@@ -302,22 +303,23 @@ void launch_bf16(const GemmArgs& base, hipStream_t st) {
   g.units = g.tiles_m * g.tiles_n;
   g.units_per_xcd = (g.units + kXcds - 1) / kXcds;
   const dim3 grid(static_cast<unsigned>(g.units_per_xcd * kXcds));
-  // two sub-slices per stage when K allows, except for the 128x128 tile, whose
-  // 96 KB ring would leave room for one block per CU
-  constexpr int SUB = BM * BN >= 128 * 128 ? 1 : kSub;
-  if (SUB > 1 && g.K % (SUB * kBK) == 0)
-    hipLaunchKernelGGL((gemm_bf16<BM, BN, SUB, kStages, CONV>), grid, dim3(kThreads), 0, st, g);
+  // Two sub-slices per stage when K allows.  The 128x128 tile then runs a
+  // 2-stage ring (64 KB), so two blocks still fit a CU.
+  constexpr int ST2 = BM * BN >= 128 * 128 ? 2 : kStages;
+  if (g.K % (kSub * kBK) == 0)
+    hipLaunchKernelGGL((gemm_bf16<BM, BN, kSub, ST2, CONV>), grid, dim3(kThreads), 0, st, g);
   else
     hipLaunchKernelGGL((gemm_bf16<BM, BN, 1, kStages, CONV>), grid, dim3(kThreads), 0, st, g);
 }
 
 // Tile shape: fewest tile-rounds per CU, weighting smaller tiles by their
-// higher LDS traffic per MFMA (measured relative cost per output element).
+// higher cost per output element (fitted to MI355X timings of the SDXL conv
+// and projection shapes: more LDS traffic per MFMA, fewer blocks per CU).
 template <bool CONV>
 void launch_bf16_auto(const GemmArgs& g, hipStream_t st) {
   const int cus = gemm_cus();
   struct Cand { int bm, bn; double cost_per_elem; };
-  const Cand cands[] = {{128, 128, 1.0}, {128, 64, 1.15}, {64, 128, 1.15}, {64, 64, 1.6}};
+  const Cand cands[] = {{128, 128, 1.0}, {128, 64, 1.27}, {64, 128, 1.23}, {64, 64, 1.57}};
   int best = 0;
   double best_cost = 1e300;
   for (int c = 0; c < 4; ++c) {
