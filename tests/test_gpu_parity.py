@@ -193,6 +193,76 @@ def test_errors_raise_before_launch():
         ops.dp_attn_stale_kv(q, q.clone(), q.clone(), 2)  # d = 48
 
 
+# ------------------------------------------------- limits and degenerate shapes
+def test_conv_max_cin_and_beyond():
+    """Cin = 2048 is the largest supported bf16 input width (the zero page
+    covers one 2048-channel pixel); one more 32-channel step is rejected."""
+    say("conv Cin=2048")
+    B, h, W, Cin, Cout = 1, 2, 6, 2048, 64
+    x = R(1, "cm.x", (B, h, W, Cin), "bf16")
+    w = R(0, "cm.w", (Cout, 3, 3, Cin), "bf16", (9 * Cin) ** -0.5)
+    ht = R(2, "cm.ht", (B, W, Cin), "bf16")
+    y = ops.dp_conv3x3_stale_halo(dev(x, "bf16"), dev(ht, "bf16"), None, dev(w, "bf16"), None)
+    assert_close(host(y), oracle.conv3x3_halo(x, ht, None, w, None), "bf16", "conv Cin=2048")
+    xb = torch.zeros((1, 1, 4, 2080), dtype=torch.bfloat16, device="cuda")
+    wb = torch.zeros((32, 3, 3, 2080), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(DPError) as e:
+        ops.dp_conv3x3_stale_halo(xb, None, None, wb, None)
+    assert e.value.status == 2
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_groupnorm_max_channels(dt):
+    """C = 2048 is the widest supported GroupNorm; C = 4096 is rejected."""
+    say("gn C=2048", dt)
+    B, T, C, G, N, rank = 2, 50, 2048, 32, 3, 2
+    x = R(1, "gm.x", (B, T, C), dt)
+    st = stale_sums_for(B, T, C, G, N, 2, dt)
+    ref, fresh = oracle.groupnorm_stale(x, st, rank, N * T, None, None, 1e-5, True, G)
+    fresh_dev = torch.empty((B, G, 2), dtype=torch.float32, device="cuda")
+    y = ops.dp_groupnorm_stale_stats(dev(x, dt), dev_f32(st), rank, N * T, None, None, 1e-5, True, G,
+                                     fresh_sums_out=fresh_dev)
+    assert_close(host(y), ref, dt, "groupnorm C=2048")
+    xb = torch.zeros((1, 4, 4096), dtype=torch.float32 if dt == "f32" else torch.bfloat16, device="cuda")
+    with pytest.raises(DPError) as e:
+        ops.dp_groupnorm_stale_stats(xb, None, 0, 4, G=32)
+    assert e.value.status == 2
+
+
+@pytest.mark.parametrize("Tq,Tkv", [(1, 20000), (1000, 65), (3, 64)])
+def test_attention_degenerate_bf16(Tq, Tkv):
+    """One query against a long (split) key range; many queries against one
+    full tile plus one ragged key; fewer queries than one wave's group."""
+    say("attn degenerate", Tq, Tkv)
+    B, H, d = 1, 2, 64
+    q = R(7, "atd.q", (B, Tq, H * d), "bf16")
+    k = R(7, "atd.k", (B, Tkv, H * d), "bf16")
+    v = R(7, "atd.v", (B, Tkv, H * d), "bf16")
+    out = ops.dp_attn_stale_kv(dev(q, "bf16"), dev(k, "bf16"), dev(v, "bf16"), H)
+    assert_close(host(out), oracle.attention(q, k, v, H), "bf16", "attention degenerate")
+
+
+def test_linear_single_row_wide_reduction():
+    say("linear M=1 Cin=4096")
+    x = R(1, "ld.x", (1, 4096), "bf16")
+    w = R(0, "ld.w", (96, 4096), "bf16", 4096 ** -0.5)
+    b = R(3, "ld.b", (96,), "f32", 0.1)
+    y = ops.dp_linear(dev(x, "bf16"), dev(w, "bf16"), dev_f32(b))
+    assert_close(host(y), oracle.linear(x, w, b), "bf16", "linear M=1")
+
+
+def test_splice_whole_buffer():
+    """The band covers every token (a single patch): the buffer becomes the
+    fresh tensor bit for bit."""
+    say("splice whole buffer")
+    B, T, C = 2, 300, 64
+    kb, vb = R(1, "sw.kb", (B, T, C), "bf16"), R(1, "sw.vb", (B, T, C), "bf16")
+    kf, vf = R(2, "sw.kf", (B, T, C), "bf16"), R(2, "sw.vf", (B, T, C), "bf16")
+    kd, vd = dev(kb, "bf16"), dev(vb, "bf16")
+    ops.dp_kv_buffer_splice(kd, vd, dev(kf, "bf16"), dev(vf, "bf16"), 0)
+    assert torch.equal(kd, dev(kf, "bf16")) and torch.equal(vd, dev(vf, "bf16"))
+
+
 # ----------------------------------------------------- full-size rank shares
 BF16_WORKLOADS = [n for n in synth.WORKLOAD_ORDER if synth.WORKLOADS[n].dtype == "bf16"]
 
