@@ -168,3 +168,71 @@ def rank_share_step(x_loc, wq, wk, wv, wo, k_buf, v_buf, t0, heads, W,
                                  eps, False, G)
     return {"attn_out": y, "k_spliced": k_s, "v_spliced": v_s, "conv_out": z.reshape(B, Tq, -1),
             "out": out, "fresh_sums": fresh}
+
+
+class DisplacedSchedule:
+    """Several denoising steps of one layer stack -- attention block, 3x3
+    conv, GroupNorm -- over N row bands, each step feeding its output to the
+    next ("DistriFusion" project summary, "How It Works": a synchronous step,
+    then steps that reuse the activations the other devices produced one step
+    earlier; "OTIL for SDXL on 4x L40S", "What is implemented where": the
+    stale state is the K/V buffers, the conv halo rows and two GroupNorm
+    scalars per group).
+
+    A synchronous step gives every band the current step's K/V rows, halo
+    rows and group sums of all bands (the unsplit computation).  A displaced
+    step gives band r its own fresh values and, for every other band, the
+    values recorded during the previous step.  Every step records its full
+    K/V buffers, each band's attention-block output rows and each band's
+    fresh group sums.
+
+    ``store(a)`` is applied wherever the device path stores a tensor (q, k,
+    v, attention output, block output, conv output, step output), and
+    ``store_sums`` to the recorded group sums (float32 on the device), so
+    that the oracle sees the same rounded operands.
+    """
+
+    def __init__(self, H, W, heads, N, weights, G=32, eps=1e-5, store=None, store_sums=None):
+        self.H, self.W, self.heads, self.N, self.G, self.eps = H, W, heads, N, G, eps
+        self.wt = {k: _f64(v) if v is not None else None for k, v in weights.items()}
+        self.store = store or (lambda a: a)
+        self.store_sums = store_sums or (lambda a: a)
+        self.bands = [partition_rows(H, N, r) for r in range(N)]
+        self.prev = None
+
+    def step(self, x, sync: bool):
+        """x [B, H*W, C] -> the next step's x; records this step's state."""
+        if not sync and self.prev is None:
+            raise ValueError("a displaced step needs a previous step")
+        x = _f64(x)
+        W, wt, s = self.W, self.wt, self.store
+        B, T, C = x.shape
+        band_x = [x[:, r0 * W:r1 * W] for r0, r1 in self.bands]
+        q = [s(linear(xb, wt["wq"])) for xb in band_x]
+        kf = [s(linear(xb, wt["wk"])) for xb in band_x]
+        vf = [s(linear(xb, wt["wv"])) for xb in band_x]
+        k_now, v_now = np.concatenate(kf, 1), np.concatenate(vf, 1)
+        ys = []
+        for r, (r0, r1) in enumerate(self.bands):
+            if sync:
+                kb, vb = k_now, v_now
+            else:
+                kb, vb = kv_buffer_splice(self.prev["k"], self.prev["v"], kf[r], vf[r], r0 * W)
+            o = s(attention(q[r], kb, vb, self.heads))
+            ys.append(s(linear(o, wt["wo"])))
+        y_src = ys if sync else self.prev["y"]
+        zs = []
+        for r, (r0, r1) in enumerate(self.bands):
+            h = r1 - r0
+            top = y_src[r - 1].reshape(B, -1, W, C)[:, -1] if r0 > 0 else None
+            bot = y_src[r + 1].reshape(B, -1, W, C)[:, 0] if r1 < self.H else None
+            z = conv3x3_halo(ys[r].reshape(B, h, W, C), top, bot, wt["conv_w"], wt["conv_b"])
+            zs.append(s(z.reshape(B, h * W, -1)))
+        sums_now = np.stack([self.store_sums(group_sums(z, self.G)) for z in zs])
+        stale = sums_now if sync else self.prev["sums"]
+        outs = []
+        for r in range(self.N):
+            out, _ = groupnorm_stale(zs[r], stale, r, T, wt["gamma"], wt["beta"], self.eps, False, self.G)
+            outs.append(s(out))
+        self.prev = {"k": k_now, "v": v_now, "y": ys, "sums": sums_now}
+        return np.concatenate(outs, 1)

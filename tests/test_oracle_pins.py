@@ -328,3 +328,82 @@ def test_rank_share_step_stale_equals_fresh_concat():
             cw, cb, stale, r, Hi * W, gamma, beta, 1e-5, G)
         outs.append(res["out"])
     np.testing.assert_allclose(np.concatenate(outs, 1), out_full, rtol=1e-9, atol=1e-10)
+
+
+# ------------------------------------------------------- multi-step schedule
+def _schedule_weights(C, seed=70):
+    return {"wq": rnd(seed, C, C, std=C ** -0.5), "wk": rnd(seed + 1, C, C, std=C ** -0.5),
+            "wv": rnd(seed + 2, C, C, std=C ** -0.5), "wo": rnd(seed + 3, C, C, std=C ** -0.5),
+            "conv_w": rnd(seed + 4, C, 3, 3, C, std=(9 * C) ** -0.5), "conv_b": rnd(seed + 5, C, std=0.1),
+            "gamma": 1 + rnd(seed + 6, C, std=0.1), "beta": rnd(seed + 7, C, std=0.1)}
+
+
+def _torch_chain(x, w, B, Hi, W, C, heads, G):
+    y = sdpa(x @ w["wq"].T, x @ w["wk"].T, x @ w["wv"].T, heads) @ w["wo"].T
+    z = torch_conv(y.reshape(B, Hi, W, C), w["conv_w"], w["conv_b"], 1).reshape(B, Hi * W, C)
+    return torch_gn(z, G, w["gamma"], w["beta"], 1e-5)
+
+
+@pytest.mark.parametrize("N", [1, 4])
+def test_schedule_sync_steps_equal_unsplit_chain(N):
+    """Synchronous steps ("DistriFusion" summary, "How It Works": the first
+    step is synchronous) over N bands equal the unsplit chain, computed by
+    torch, applied step after step."""
+    B, Hi, W, C, heads, G = 2, 8, 4, 16, 2, 4
+    w = _schedule_weights(C)
+    sch = oracle.DisplacedSchedule(Hi, W, heads, N, w, G=G)
+    x = ref = rnd(80, B, Hi * W, C)
+    for _ in range(3):
+        x = sch.step(x, True)
+        ref = _torch_chain(ref, w, B, Hi, W, C, heads, G)
+        np.testing.assert_allclose(x, ref, rtol=1e-9, atol=1e-10)
+
+
+def test_schedule_single_band_displaced_equals_sync():
+    """With one band nothing is stale: displaced steps equal the chain."""
+    B, Hi, W, C, heads, G = 1, 6, 4, 16, 2, 4
+    w = _schedule_weights(C, 90)
+    sch = oracle.DisplacedSchedule(Hi, W, heads, 1, w, G=G)
+    x = ref = rnd(91, B, Hi * W, C)
+    for s in range(3):
+        x = sch.step(x, s == 0)
+        ref = _torch_chain(ref, w, B, Hi, W, C, heads, G)
+        np.testing.assert_allclose(x, ref, rtol=1e-9, atol=1e-10)
+
+
+def test_schedule_displaced_with_unchanged_input_equals_sync():
+    """When the activations did not change between steps, the state recorded
+    one step earlier is the current state, so a displaced step reproduces the
+    synchronous one."""
+    B, Hi, W, C, heads, G, N = 2, 8, 4, 16, 2, 4, 4
+    w = _schedule_weights(C, 100)
+    x = rnd(101, B, Hi * W, C)
+    sch = oracle.DisplacedSchedule(Hi, W, heads, N, w, G=G)
+    sync_out = sch.step(x, True)
+    disp_out = sch.step(x, False)
+    np.testing.assert_allclose(disp_out, sync_out, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(disp_out, _torch_chain(x, w, B, Hi, W, C, heads, G), rtol=1e-9, atol=1e-10)
+
+
+def test_schedule_displaced_step_reads_other_bands_from_previous_step():
+    """In a displaced step, band r's output depends on the other bands' current
+    activations only through the previous step's state: perturbing band p's
+    input right before the step changes band p's output and no other band's.
+    A synchronous step propagates the perturbation."""
+    B, Hi, W, C, heads, G, N = 1, 8, 4, 16, 2, 4, 4
+    w = _schedule_weights(C, 110)
+    x0 = rnd(111, B, Hi * W, C)
+    p = 2
+    r0, r1 = oracle.partition_rows(Hi, N, p)
+    for sync in (False, True):
+        outs = []
+        for delta in (0.0, 0.5):
+            sch = oracle.DisplacedSchedule(Hi, W, heads, N, w, G=G)
+            x1 = sch.step(x0, True)
+            x1[:, r0 * W:r1 * W] += delta
+            outs.append(sch.step(x1, sync))
+        changed = np.abs(outs[0] - outs[1]).reshape(B, Hi, W, C).max(axis=(0, 2, 3)) > 0
+        if sync:
+            assert changed.sum() > r1 - r0  # other bands see the perturbation
+        else:
+            assert changed[r0:r1].all() and not changed[:r0].any() and not changed[r1:].any()
