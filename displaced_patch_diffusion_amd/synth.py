@@ -254,3 +254,24 @@ def stale_noise(w: Workload, name: str, shape) -> np.ndarray:
 
 def random_tensor(seed: int, name: str, shape, dtype: str, std: float = 1.0) -> np.ndarray:
     return as_storage(normal(seed, name, shape, std), dtype)
+
+
+def schedule_inputs(w: Workload) -> dict:
+    """Initial full-image activations [B, H*W, C] and the weights of one layer
+    stack (projections, conv, GroupNorm affine) for the multi-step schedule of
+    a single-level workload; the same names and seeds as the per-op inputs."""
+    if w.two_level:
+        raise ValueError("the multi-step schedule runs single-level workloads")
+    B, H, W, C, dt = w.B, w.attn_H, w.attn_W, w.attn_C, w.dtype
+    s = 1.0 / np.sqrt(C)
+    return {
+        "x0": as_storage(normal(SEED_ACTIVATIONS, "attn.x_full", (B, H * W, C)), dt),
+        "wq": as_storage(normal(SEED_WEIGHTS, "attn.wq", (C, C), s), dt),
+        "wk": as_storage(normal(SEED_WEIGHTS, "attn.wk", (C, C), s), dt),
+        "wv": as_storage(normal(SEED_WEIGHTS, "attn.wv", (C, C), s), dt),
+        "wo": as_storage(normal(SEED_WEIGHTS, "attn.wo", (C, C), s), dt),
+        "conv_w": as_storage(normal(SEED_WEIGHTS, "conv0.w", (C, 3, 3, C), 1.0 / np.sqrt(9 * C)), dt),
+        "conv_b": normal(SEED_AFFINE, "conv0.bias", (C,), 0.1),
+        "gamma": normal(SEED_AFFINE, "gn0.gamma", (C,), 0.1, 1.0),
+        "beta": normal(SEED_AFFINE, "gn0.beta", (C,), 0.1),
+    }

@@ -200,8 +200,10 @@ class DisplacedSchedule:
         self.bands = [partition_rows(H, N, r) for r in range(N)]
         self.prev = None
 
-    def step(self, x, sync: bool):
-        """x [B, H*W, C] -> the next step's x; records this step's state."""
+    def step(self, x, sync: bool, alpha: float = 1.0):
+        """x [B, H*W, C] -> x + alpha (stack(x) - x), the synthetic sampler
+        update between steps (alpha = 1: the stack's output); records this
+        step's state."""
         if not sync and self.prev is None:
             raise ValueError("a displaced step needs a previous step")
         x = _f64(x)
@@ -235,4 +237,5 @@ class DisplacedSchedule:
             out, _ = groupnorm_stale(zs[r], stale, r, T, wt["gamma"], wt["beta"], self.eps, False, self.G)
             outs.append(s(out))
         self.prev = {"k": k_now, "v": v_now, "y": ys, "sums": sums_now}
-        return np.concatenate(outs, 1)
+        out = np.concatenate(outs, 1)
+        return out if alpha == 1.0 else s(x + alpha * (out - x))

@@ -407,3 +407,16 @@ def test_schedule_displaced_step_reads_other_bands_from_previous_step():
             assert changed.sum() > r1 - r0  # other bands see the perturbation
         else:
             assert changed[r0:r1].all() and not changed[:r0].any() and not changed[r1:].any()
+
+
+def test_schedule_sampler_update_single_band_equals_torch():
+    """The sampler update x + alpha (stack(x) - x) between steps, one band
+    (nothing stale): equal to the torch chain blended the same way."""
+    B, Hi, W, C, heads, G, a = 1, 6, 4, 16, 2, 4, 0.3
+    w = _schedule_weights(C, 120)
+    sch = oracle.DisplacedSchedule(Hi, W, heads, 1, w, G=G)
+    x = ref = rnd(121, B, Hi * W, C)
+    for s in range(3):
+        x = sch.step(x, s == 0, a)
+        ref = ref + a * (_torch_chain(ref, w, B, Hi, W, C, heads, G) - ref)
+        np.testing.assert_allclose(x, ref, rtol=1e-9, atol=1e-10)
