@@ -2,8 +2,10 @@
 """Benchmark of one rank's share of a displaced-patch diffusion step on one MI355X.
 
 One step = every hot-path op of the share, in order, through libdp:
-  single-level workloads: Q/K/V projections of the local rows -> K/V buffer
-      splice -> attention over the full-image buffer -> output projection ->
+  single-level workloads: Q/K/V projections of the local rows with K/V
+      written into the full-image buffers (one launch by default; --qkv
+      separate runs three projections and then the K/V buffer splice) ->
+      attention over the full-image buffer -> output projection ->
       conv3x3 with stale halo rows -> GroupNorm with stale remote sums;
   two-level workload: GN+SiLU -> conv -> GN+SiLU -> conv at the conv level, and
       projections -> splice -> attention -> output projection at the
@@ -45,6 +47,8 @@ def log(*a):
 # ----------------------------------------------------------------- GPU state
 class Share:
     """Device tensors of one rank's share plus its stale state."""
+
+    fused_qkv = True
 
     def __init__(self, w, torch, ops, synth):
         self.w, self.torch, self.ops = w, torch, ops
@@ -186,12 +190,18 @@ class Share:
                                           ci["b"], y=self.zc[i].view(B, hc, Wc, Cc))
                 mark("conv")
                 x = self.zc[i]
-        ops.dp_linear(self.x_loc, self.wq, y=self.q)
-        ops.dp_linear(self.x_loc, self.wk, y=self.kf)
-        ops.dp_linear(self.x_loc, self.wv, y=self.vf)
-        mark("proj")
-        ops.dp_kv_buffer_splice(self.k_buf, self.v_buf, self.kf, self.vf, self.t0)
-        mark("splice")
+        if self.fused_qkv:
+            # one launch: Q/K/V of the local rows, K and V written into the buffers
+            ops.dp_qkv_projection_into_buffers(self.x_loc, self.wq, self.wk, self.wv, self.k_buf,
+                                               self.v_buf, self.t0, q=self.q)
+            mark("proj")
+        else:
+            ops.dp_linear(self.x_loc, self.wq, y=self.q)
+            ops.dp_linear(self.x_loc, self.wk, y=self.kf)
+            ops.dp_linear(self.x_loc, self.wv, y=self.vf)
+            mark("proj")
+            ops.dp_kv_buffer_splice(self.k_buf, self.v_buf, self.kf, self.vf, self.t0)
+            mark("splice")
         ops.dp_attn_stale_kv(self.q, self.k_buf, self.v_buf, w.heads, out=self.o, ws=self.attn_ws)
         mark("attn")
         ops.dp_linear(self.o, self.wo, y=self.y)
@@ -310,6 +320,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle's attention sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--qkv", choices=("fused", "separate"), default="fused",
+                    help="fused: one launch projects Q/K/V and writes K/V into the buffers; "
+                         "separate: three projections then the K/V splice")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -328,6 +341,7 @@ def main():
     torch.cuda.set_device(0)
     log(f"bench: workload {w.name}: building inputs")
     share = Share(w, torch, ops, synth)
+    share.fused_qkv = args.qkv == "fused"
 
     names = []
 
@@ -390,7 +404,8 @@ def main():
         "config": {"workload": w.name, "batch": w.B, "attn_level": f"{w.attn_H}x{w.attn_W}",
                    "C_attn": w.attn_C, "heads": w.heads, "head_dim": w.head_dim,
                    "conv_level": f"{w.conv_H}x{w.conv_W}", "C_conv": w.conv_C, "n_patches": w.N,
-                   "rank": w.rank, "Tq": w.Tq, "T_kv": w.T_kv, "parallelism": "one rank's share, 1 GPU"},
+                   "rank": w.rank, "Tq": w.Tq, "T_kv": w.T_kv, "qkv": args.qkv,
+                   "parallelism": "one rank's share, 1 GPU"},
         "roofline": roofline,
         "kernels": kern,
         "groupnorm_GBps": kern.get("groupnorm", {}).get("GB/s"),

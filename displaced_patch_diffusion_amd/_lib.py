@@ -28,6 +28,7 @@ SIGNATURES = {
     "dp_groupnorm_stale_stats": (INT, [P, P, I64, I64, I64, P, P, F32, INT, P, P, I64, I64, I64,
                                        I64, INT, P, SZ, P]),
     "dp_linear": (INT, [P, P, P, P, I64, I64, I64, INT, P]),
+    "dp_qkv_projection_into_buffers": (INT, [P, P, P, P, P, P, P, I64, I64, I64, I64, I64, INT, P]),
 }
 
 DP_OK, DP_ERR_INVALID_ARG, DP_ERR_UNSUPPORTED, DP_ERR_HIP = 0, 1, 2, 3

@@ -45,12 +45,30 @@ struct ConvGeom {
   int h, W, Cin;
 };
 
+// Output columns come in segments of seg_n (n_seg of them, N = n_seg * seg_n).
+// Column n of segment s = n / seg_n takes its weight row from wts[s] (row
+// n - s*seg_n) and its result goes to outs[s], column n - s*seg_n (leading
+// dimension seg_n), output row (m / rpg) * grp_rows[s] + row_off[s] + m % rpg.
+// A plain GEMM is one segment with rpg = grp_rows = M and row_off = 0; the
+// fused Q/K/V projection is three, K and V landing at rows t0 + i of every
+// batch item's full-image buffer.
+struct OutMap {
+  const void* wts[3];
+  void* outs[3];
+  int n_seg, seg_n, rpg;
+  int grp_rows[3], row_off[3];
+};
+
+__device__ __forceinline__ int64_t out_row(const OutMap& o, int s, int m) {
+  const int g = m / o.rpg;
+  return static_cast<int64_t>(g) * o.grp_rows[s] + o.row_off[s] + (m - g * o.rpg);
+}
+
 struct GemmArgs {
   const bf16_t* a;     // dense rows [M, K] (projections)
   ConvGeom geo;        // implicit im2col (conv)
-  const bf16_t* wt;    // [N, K]
+  OutMap map;          // weights [N, K] by segment, outputs
   const float* bias;   // [N] or null
-  bf16_t* y;           // [M, N]
   int M, N, K;
   int tiles_m, tiles_n, units, units_per_xcd;
 };
@@ -118,7 +136,10 @@ __global__ void __launch_bounds__(kThreads, 2) gemm_bf16(GemmArgs g) {
     const int row = 16 * (4 * j + wave) + (lane >> 2);
     const int chunk = (lane & 3) ^ gswz(row);
     const int n = min(n0 + row, g.N - 1);  // rows past N repeat the last one; never stored
-    bsrc[j] = reinterpret_cast<const char*>(g.wt + static_cast<int64_t>(n) * g.K) + chunk * 16;
+    const int seg = n / g.map.seg_n;
+    bsrc[j] = reinterpret_cast<const char*>(static_cast<const bf16_t*>(g.map.wts[seg]) +
+                                            static_cast<int64_t>(n - seg * g.map.seg_n) * g.K) +
+              chunk * 16;
   }
   const char* asrc[kASlabs];
   int a_b[kASlabs], a_i[kASlabs], a_c[kASlabs], a_chunk[kASlabs];
@@ -265,6 +286,9 @@ __global__ void __launch_bounds__(kThreads, 2) gemm_bf16(GemmArgs g) {
       const int m = m0 + wm * WM + 32 * j + l32;
       const int nblk = n0 + wn * WN + 32 * i;
       if (m >= g.M || nblk >= g.N) continue;
+      const int seg = nblk / g.map.seg_n;  // a 32-column block lies in one segment
+      bf16_t* yrow = static_cast<bf16_t*>(g.map.outs[seg]) + out_row(g.map, seg, m) * g.map.seg_n -
+                     seg * g.map.seg_n;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int n = nblk + 8 * q + 4 * gq;
@@ -272,7 +296,7 @@ __global__ void __launch_bounds__(kThreads, 2) gemm_bf16(GemmArgs g) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * q + e] + (g.bias ? g.bias[n + e] : 0.f);
         u32x2 packed = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-        *reinterpret_cast<u32x2*>(g.y + static_cast<int64_t>(m) * g.N + n) = packed;
+        *reinterpret_cast<u32x2*>(yrow + n) = packed;
       }
     }
 }
@@ -366,8 +390,8 @@ __device__ __forceinline__ float a_elem_f32(const float* a, const float* x, cons
 template <bool CONV>
 __global__ void __launch_bounds__(kThreads)
 gemm_f32(const float* __restrict__ a, const float* __restrict__ x, const float* __restrict__ ht,
-         const float* __restrict__ hb, int h, int W, int Cin, const float* __restrict__ wt,
-         const float* __restrict__ bias, float* __restrict__ y, int M, int N, int K) {
+         const float* __restrict__ hb, int h, int W, int Cin, OutMap map,
+         const float* __restrict__ bias, int M, int N, int K) {
   __shared__ float As[kFK][kFT + 1];
   __shared__ float Bs[kFK][kFT + 1];
   const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
@@ -380,7 +404,12 @@ gemm_f32(const float* __restrict__ a, const float* __restrict__ x, const float* 
       const int r = e / kFK, kk = e % kFK;
       As[kk][r] = a_elem_f32<CONV>(a, x, ht, hb, h, W, Cin, m0 + r, k0 + kk, M, K);
       const int n = n0 + r, k = k0 + kk;
-      Bs[kk][r] = (n < N && k < K) ? wt[static_cast<int64_t>(n) * K + k] : 0.f;
+      float bv = 0.f;
+      if (n < N && k < K) {
+        const int seg = n / map.seg_n;
+        bv = static_cast<const float*>(map.wts[seg])[static_cast<int64_t>(n - seg * map.seg_n) * K + k];
+      }
+      Bs[kk][r] = bv;
     }
     __syncthreads();
 #pragma unroll
@@ -402,18 +431,35 @@ gemm_f32(const float* __restrict__ a, const float* __restrict__ x, const float* 
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int m = m0 + ty + 16 * i, n = n0 + tx + 16 * j;
-      if (m < M && n < N) y[static_cast<int64_t>(m) * N + n] = acc[i][j] + (bias ? bias[n] : 0.f);
+      if (m < M && n < N) {
+        const int seg = n / map.seg_n;
+        static_cast<float*>(map.outs[seg])[out_row(map, seg, m) * map.seg_n + n - seg * map.seg_n] =
+            acc[i][j] + (bias ? bias[n] : 0.f);
+      }
     }
 }
 
+// A plain GEMM's output map: one segment, rows as computed.
+OutMap plain_map(const void* wt, void* y, int64_t M, int64_t N) {
+  OutMap m{};
+  m.wts[0] = wt;
+  m.outs[0] = y;
+  m.n_seg = 1;
+  m.seg_n = static_cast<int>(N);
+  m.rpg = static_cast<int>(M);
+  m.grp_rows[0] = static_cast<int>(M);
+  m.row_off[0] = 0;
+  return m;
+}
+
 dp_status run_gemm(bool conv, const void* a, const void* x, const void* ht, const void* hb, int h,
-                   int W, int Cin, const void* wt, const float* bias, void* y, int64_t M,
-                   int64_t N, int64_t K, dp_dtype dt, hipStream_t st, const char* name) {
+                   int W, int Cin, const OutMap& map, const float* bias, int64_t M, int64_t N,
+                   int64_t K, dp_dtype dt, hipStream_t st, const char* name) {
   if (M > 0x7FFFFFFF || N > 0x7FFFFFFF || K > 0x7FFFFFFF)
     return dp::fail(DP_ERR_UNSUPPORTED, "%s: dimension exceeds 2^31", name);
   dp::clear_error();
   if (dt == DP_BF16) {
-    if (K % kBK != 0 || N % 32 != 0 || (conv && (Cin % kBK != 0 || Cin > 2048)))
+    if (K % kBK != 0 || map.seg_n % 32 != 0 || (conv && (Cin % kBK != 0 || Cin > 2048)))
       return dp::fail(DP_ERR_UNSUPPORTED, "%s: bf16 path needs Cin %% 32 == 0 (conv: Cin <= 2048) and Cout %% 32 == 0", name);
     if ((M + 63) / 64 * ((N + 63) / 64) > 0x3FFFFFFF)
       return dp::fail(DP_ERR_UNSUPPORTED, "%s: too many tiles", name);
@@ -421,9 +467,8 @@ dp_status run_gemm(bool conv, const void* a, const void* x, const void* ht, cons
     g.a = static_cast<const bf16_t*>(a);
     g.geo = ConvGeom{static_cast<const bf16_t*>(x), static_cast<const bf16_t*>(ht),
                      static_cast<const bf16_t*>(hb), h, W, Cin};
-    g.wt = static_cast<const bf16_t*>(wt);
+    g.map = map;
     g.bias = bias;
-    g.y = static_cast<bf16_t*>(y);
     g.M = (int)M;
     g.N = (int)N;
     g.K = (int)K;
@@ -436,13 +481,11 @@ dp_status run_gemm(bool conv, const void* a, const void* x, const void* ht, cons
     if (conv)
       hipLaunchKernelGGL(gemm_f32<true>, grid, dim3(kThreads), 0, st, nullptr,
                          static_cast<const float*>(x), static_cast<const float*>(ht),
-                         static_cast<const float*>(hb), h, W, Cin, static_cast<const float*>(wt),
-                         bias, static_cast<float*>(y), (int)M, (int)N, (int)K);
+                         static_cast<const float*>(hb), h, W, Cin, map, bias, (int)M, (int)N, (int)K);
     else
       hipLaunchKernelGGL(gemm_f32<false>, grid, dim3(kThreads), 0, st,
-                         static_cast<const float*>(a), nullptr, nullptr, nullptr, 0, 0, 0,
-                         static_cast<const float*>(wt), bias, static_cast<float*>(y), (int)M,
-                         (int)N, (int)K);
+                         static_cast<const float*>(a), nullptr, nullptr, nullptr, 0, 0, 0, map, bias,
+                         (int)M, (int)N, (int)K);
   }
   return dp::check_launch(name);
 }
@@ -458,8 +501,8 @@ DP_API dp_status dp_linear(const void* x, const void* w, const float* bias, void
   const size_t es = dp::dtype_size(dt);
   if (dp::overlaps(x, M * Cin * es, y, M * Cout * es) || dp::overlaps(w, Cout * Cin * es, y, M * Cout * es))
     return fail(DP_ERR_INVALID_ARG, "dp_linear: output overlaps an input");
-  return run_gemm(false, x, nullptr, nullptr, nullptr, 0, 0, 0, w, bias, y, M, Cout, Cin, dt, stream,
-                  "dp_linear");
+  return run_gemm(false, x, nullptr, nullptr, nullptr, 0, 0, 0, plain_map(w, y, M, Cout), bias, M, Cout,
+                  Cin, dt, stream, "dp_linear");
 }
 
 DP_API dp_status dp_conv3x3_stale_halo(const void* x, const void* halo_top, const void* halo_bot,
@@ -479,6 +522,49 @@ DP_API dp_status dp_conv3x3_stale_halo(const void* x, const void* halo_top, cons
     return fail(DP_ERR_INVALID_ARG, "dp_conv3x3_stale_halo: output overlaps an input");
   if (h > 0x7FFFFFFF || W > 0x7FFFFFFF || Cin > 0x7FFFFFFF)
     return fail(DP_ERR_UNSUPPORTED, "dp_conv3x3_stale_halo: dimension exceeds 2^31");
-  return run_gemm(true, nullptr, x, halo_top, halo_bot, (int)h, (int)W, (int)Cin, w, bias, y,
-                  B * h * W, Cout, 9 * Cin, dt, stream, "dp_conv3x3_stale_halo");
+  return run_gemm(true, nullptr, x, halo_top, halo_bot, (int)h, (int)W, (int)Cin,
+                  plain_map(w, y, B * h * W, Cout), bias, B * h * W, Cout, 9 * Cin, dt, stream,
+                  "dp_conv3x3_stale_halo");
+}
+
+DP_API dp_status dp_qkv_projection_into_buffers(const void* x, const void* wq, const void* wk,
+                                                const void* wv, void* q, void* k_buf, void* v_buf,
+                                                int64_t B, int64_t T_loc, int64_t T_kv, int64_t t0,
+                                                int64_t C, dp_dtype dt, hipStream_t stream) {
+  using dp::fail;
+  const char* name = "dp_qkv_projection_into_buffers";
+  if (!x || !wq || !wk || !wv || !q || !k_buf || !v_buf) return fail(DP_ERR_INVALID_ARG, "%s: NULL pointer", name);
+  if (B <= 0 || T_loc <= 0 || T_kv <= 0 || C <= 0) return fail(DP_ERR_INVALID_ARG, "%s: sizes must be positive", name);
+  if (t0 < 0 || t0 + T_loc > T_kv) return fail(DP_ERR_INVALID_ARG, "%s: rows [t0, t0+T_loc) outside [0, T_kv)", name);
+  if (!dp::dtype_ok(dt)) return fail(DP_ERR_INVALID_ARG, "%s: bad dtype", name);
+  if (B * T_kv > 0x7FFFFFFF || 3 * C > 0x7FFFFFFF) return fail(DP_ERR_UNSUPPORTED, "%s: dimension exceeds 2^31", name);
+  const size_t es = dp::dtype_size(dt);
+  const size_t xb = static_cast<size_t>(B * T_loc * C) * es, bb = static_cast<size_t>(B * T_kv * C) * es;
+  const size_t wb = static_cast<size_t>(C * C) * es;
+  const void* ins[4] = {x, wq, wk, wv};
+  const size_t insz[4] = {xb, wb, wb, wb};
+  void* outs[3] = {q, k_buf, v_buf};
+  const size_t outsz[3] = {xb, bb, bb};
+  for (int o = 0; o < 3; ++o) {
+    for (int i = 0; i < 4; ++i)
+      if (dp::overlaps(ins[i], insz[i], outs[o], outsz[o])) return fail(DP_ERR_INVALID_ARG, "%s: an output overlaps an input", name);
+    for (int p = o + 1; p < 3; ++p)
+      if (dp::overlaps(outs[p], outsz[p], outs[o], outsz[o])) return fail(DP_ERR_INVALID_ARG, "%s: outputs overlap", name);
+  }
+  OutMap m{};
+  m.wts[0] = wq;
+  m.wts[1] = wk;
+  m.wts[2] = wv;
+  m.outs[0] = q;
+  m.outs[1] = k_buf;
+  m.outs[2] = v_buf;
+  m.n_seg = 3;
+  m.seg_n = static_cast<int>(C);
+  m.rpg = static_cast<int>(T_loc);
+  m.grp_rows[0] = static_cast<int>(T_loc);
+  m.row_off[0] = 0;
+  m.grp_rows[1] = m.grp_rows[2] = static_cast<int>(T_kv);
+  m.row_off[1] = m.row_off[2] = static_cast<int>(t0);
+  return run_gemm(false, x, nullptr, nullptr, nullptr, 0, 0, 0, m, nullptr, B * T_loc, 3 * C, C, dt, stream,
+                  name);
 }

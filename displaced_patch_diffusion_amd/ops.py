@@ -137,3 +137,22 @@ def dp_linear(x, w, bias=None, y=None):
         y = torch.empty(x.shape[:-1] + (Cout,), dtype=x.dtype, device=x.device)
     check(lib().dp_linear(_p(x), _p(w), _p(bias), _p(y), M, Cin, Cout, dt, _stream()), "dp_linear")
     return y
+
+
+def dp_qkv_projection_into_buffers(x, wq, wk, wv, k_buf, v_buf, t0: int, q=None):
+    """x [B,T_loc,C] -> q [B,T_loc,C]; K/V rows written into k_buf/v_buf [B,T_kv,C]
+    at tokens [t0, t0+T_loc) (in place).  Returns q."""
+    _dev(x, wq, wk, wv, k_buf, v_buf, q)
+    dt = _dt(x, wq, wk, wv, k_buf, v_buf, q)
+    B, T_loc, C = x.shape
+    T_kv = k_buf.shape[1]
+    if k_buf.shape != (B, T_kv, C) or v_buf.shape != k_buf.shape:
+        raise ValueError("k_buf/v_buf must be [B,T_kv,C] with x's B and C")
+    if any(w.shape != (C, C) for w in (wq, wk, wv)):
+        raise ValueError("weights must be [C,C]")
+    if q is None:
+        q = torch.empty_like(x)
+    check(lib().dp_qkv_projection_into_buffers(_p(x), _p(wq), _p(wk), _p(wv), _p(q), _p(k_buf),
+                                               _p(v_buf), B, T_loc, T_kv, t0, C, dt, _stream()),
+          "dp_qkv_projection_into_buffers")
+    return q

@@ -157,6 +157,29 @@ dp_status dp_groupnorm_stale_stats(const void* x, const float* stale_sums, int64
 dp_status dp_linear(const void* x, const void* w, const float* bias, void* y, int64_t M,
                     int64_t Cin, int64_t Cout, dp_dtype dt, hipStream_t stream);
 
+/*
+ * Fused Q/K/V projection of the rank's rows, with K and V written straight
+ * into the full-image buffers: the projections and the K/V splice in one
+ * launch (the displaced attention's buffers hold the rank's fresh rows and
+ * everyone else's stale rows: "OTIL ...", "What is implemented where"; xDiT
+ * issue thread, maintainer's first reply).  For b in [0, B), i in [0, T_loc):
+ *   q[b, i, :]          = x[b, i, :] . Wq^T
+ *   k_buf[b, t0 + i, :] = x[b, i, :] . Wk^T
+ *   v_buf[b, t0 + i, :] = x[b, i, :] . Wv^T
+ * Every other row of k_buf and v_buf is left untouched.  Each value is the
+ * one dp_linear computes (same reduction order), so the call equals three
+ * dp_linear calls followed by dp_kv_buffer_splice, bit for bit.
+ * x, q [B, T_loc, C]; wq, wk, wv [C, C]; k_buf, v_buf [B, T_kv, C]; no bias.
+ * Supported: bf16 with C % 32 == 0; f32 any C.
+ * Errors: INVALID_ARG for NULL pointers, sizes <= 0, t0 < 0 or
+ * t0 + T_loc > T_kv, or outputs overlapping inputs or each other;
+ * UNSUPPORTED for other shapes.
+ */
+dp_status dp_qkv_projection_into_buffers(const void* x, const void* wq, const void* wk,
+                                         const void* wv, void* q, void* k_buf, void* v_buf,
+                                         int64_t B, int64_t T_loc, int64_t T_kv, int64_t t0,
+                                         int64_t C, dp_dtype dt, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

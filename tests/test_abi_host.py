@@ -125,3 +125,21 @@ def test_groupnorm_validation(lib):
     need2 = lib.dp_groupnorm_stale_stats_workspace(2, 7200, 4096, 32)
     assert call(C=4096, ws_bytes=need2) == _lib.DP_ERR_UNSUPPORTED
     assert call(y=A + 2) == _lib.DP_ERR_INVALID_ARG
+
+
+def test_qkv_projection_validation(lib):
+    F, G2, H2 = 0x60000000, 0x70000000, 0x80000000
+    f = lib.dp_qkv_projection_into_buffers
+    # rows [t0, t0 + T_loc) must lie inside the buffer
+    st, _ = status_and_error(f, A, Bp, Cp, D, E, F, G2, 2, 64, 256, 200, 64, _lib.DP_BF16, None)
+    assert st == _lib.DP_ERR_INVALID_ARG
+    st, _ = status_and_error(f, A, Bp, Cp, D, E, F, G2, 2, 64, 256, -1, 64, _lib.DP_BF16, None)
+    assert st == _lib.DP_ERR_INVALID_ARG
+    st, _ = status_and_error(f, A, Bp, Cp, None, E, F, G2, 2, 64, 256, 0, 64, _lib.DP_BF16, None)
+    assert st == _lib.DP_ERR_INVALID_ARG
+    # the two buffers may not overlap each other
+    st, msg = status_and_error(f, A, Bp, Cp, D, E, F, F + 64, 2, 64, 256, 0, 64, _lib.DP_BF16, None)
+    assert st == _lib.DP_ERR_INVALID_ARG and "overlap" in msg
+    # bf16 needs C % 32 == 0
+    st, _ = status_and_error(f, A, Bp, Cp, D, E, F, H2, 2, 64, 256, 0, 48, _lib.DP_BF16, None)
+    assert st == _lib.DP_ERR_UNSUPPORTED

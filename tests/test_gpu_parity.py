@@ -418,3 +418,29 @@ def test_stale_equals_fresh_ranks_concat_on_gpu():
     # the one for a share (1024 queries), so the summation order differs: the
     # property holds to the bf16 tolerance, not bit for bit.
     assert_close(host(cat), host(ref), "bf16", "stale==fresh concatenation")
+
+
+# ------------------------------------------- fused Q/K/V projection (NEXT-2)
+@pytest.mark.parametrize("dt,B,T_kv,C,t0,T_loc", [
+    ("bf16", 2, 1000, 640, 300, 200), ("bf16", 1, 96, 64, 0, 96), ("bf16", 2, 333, 320, 250, 83),
+    ("f32", 2, 256, 64, 64, 64), ("f32", 1, 50, 12, 40, 10),
+])
+def test_qkv_projection_into_buffers(dt, B, T_kv, C, t0, T_loc):
+    """Equals dp_linear x3 + dp_kv_buffer_splice bit for bit (rows outside
+    the band untouched), and the oracle's projections within tolerance."""
+    say("qkv fused", dt, B, T_kv, C, t0, T_loc)
+    x = R(1, "qkv.x", (B, T_loc, C), dt)
+    ws = [R(0, f"qkv.w{i}", (C, C), dt, C ** -0.5) for i in range(3)]
+    kb, vb = R(2, "qkv.kb", (B, T_kv, C), dt), R(2, "qkv.vb", (B, T_kv, C), dt)
+    xd, wd = dev(x, dt), [dev(w, dt) for w in ws]
+    k1, v1 = dev(kb, dt), dev(vb, dt)
+    q1 = ops.dp_qkv_projection_into_buffers(xd, wd[0], wd[1], wd[2], k1, v1, t0)
+    k2, v2 = dev(kb, dt), dev(vb, dt)
+    q2 = ops.dp_linear(xd, wd[0])
+    ops.dp_kv_buffer_splice(k2, v2, ops.dp_linear(xd, wd[1]), ops.dp_linear(xd, wd[2]), t0)
+    assert torch.equal(q1, q2) and torch.equal(k1, k2) and torch.equal(v1, v2)
+    assert_close(host(q1), oracle.linear(x, ws[0]), dt, "fused q")
+    assert_close(host(k1[:, t0:t0 + T_loc]), oracle.linear(x, ws[1]), dt, "fused k")
+    assert_close(host(v1[:, t0:t0 + T_loc]), oracle.linear(x, ws[2]), dt, "fused v")
+    outside = np.r_[0:t0, t0 + T_loc:T_kv]
+    assert np.array_equal(host(k1)[:, outside], np.asarray(kb, np.float64)[:, outside])
