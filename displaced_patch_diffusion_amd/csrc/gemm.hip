@@ -10,13 +10,12 @@
 // Reduction index of the conv: k = tap * Cin + c with tap = (dy+1)*3 + (dx+1),
 // matching the [Cout, 3, 3, Cin] weight layout, so weight rows are K-contiguous.
 //
-// bf16 path (gfx950): a 256-thread block computes a 128x128, 128x64, 64x128 or
-// 64x64 output tile (chosen per problem so the tiles spread evenly over the
-// CUs); tiles sharing A rows are dealt to one XCD.  K moves through a 3-stage
-// LDS ring (2 stages for the 128x128 tile) by direct global->LDS loads issued
-// ahead; a stage holds two 32-wide sub-slices (one when K is not a multiple of
-// 64), so each barrier covers 64 of K.  Sub-slice rows are 64 bytes,
-// XOR-swizzled.  Each wave owns a quarter of the tile as
+// bf16 path (gfx950): a 256-thread block computes one output tile of a shape
+// chosen per problem so the tiles spread evenly over the CUs (128x128, 64x128,
+// 64x64, 160x128, 96x128 or 128x160); tiles sharing A rows are dealt to one
+// XCD.  K moves through an LDS ring by direct global->LDS loads issued ahead, 64
+// of K per stage (128-byte rows, one L2 line each) or 32 when K or Cin is not a
+// multiple of 64.  LDS rows are XOR-swizzled.  Each wave owns a quarter of the tile as
 // v_mfma_f32_32x32x16_bf16 blocks computed as (W rows) x (A rows)^T, so an
 // accumulator lane holds 4 consecutive output channels of one output row and
 // the epilogue writes 8-byte runs.
@@ -28,9 +27,8 @@
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kBK = 32;            // reduction sub-slice (64 bytes of bf16 per row)
-constexpr int kSub = 2;            // sub-slices per ring stage when K allows (64 of K per barrier)
-constexpr int kStages = 3;         // LDS ring depth (loads run two stages ahead)
+constexpr int kBK = 32;            // narrowest reduction slice (64 bytes of bf16 per row)
+constexpr int kStages = 3;         // LDS ring depth of the narrow-slice fallback
 constexpr int kXcds = 8;
 
 // Zero page read by padding rows of the implicit im2col (columns outside the
@@ -73,10 +71,14 @@ struct GemmArgs {
   int tiles_m, tiles_n, units, units_per_xcd;
 };
 
-// 64-byte LDS rows: 16-byte chunk c of row r lives in slot c ^ ((r >> 2) & 3),
-// which keeps the operand reads (16 consecutive rows, one chunk) and the DMA
-// writes free of bank conflicts.
-__device__ __forceinline__ int gswz(int row) { return (row >> 2) & 3; }
+// LDS rows of 64 bytes (BK = 32) or 128 bytes (BK = 64): 16-byte chunk c of
+// row r lives in slot c ^ swz(r), chosen so the 16 rows one operand read
+// touches per LDS cycle (same chunk) hit 16 distinct 4-bank groups of the 64
+// banks, and the DMA writes (1 KB contiguous) are conflict-free.
+template <int BK>
+__device__ __forceinline__ int swz(int row) {
+  return BK == 64 ? (row >> 1) & 7 : (row >> 2) & 3;
+}
 
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"  // m0 is written on purpose; nothing else here uses it
@@ -86,7 +88,7 @@ __device__ __forceinline__ int gswz(int row) { return (row >> 2) & 3; }
 __device__ __forceinline__ void gdma16(const void* gsrc, unsigned int m0) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
                :
-               : "s"(m0), "v"(gsrc)
+               : "s"(__builtin_amdgcn_readfirstlane(m0)), "v"(gsrc)
                : "memory", "m0");
 }
 #pragma clang diagnostic pop
@@ -102,133 +104,142 @@ struct Stage {
   static constexpr int value = S;
 };
 
-// One block computes a BM x BN output tile with 4 waves arranged 2 x 2; each
-// wave owns (BM/2) x (BN/2) as 32 x 32 MFMA blocks computed as (W rows) x
-// (A rows)^T, so an accumulator lane holds 4 consecutive output channels of one
-// output row.  K advances SUB 32-wide sub-slices per stage through an ST-stage
-// LDS ring.
-template <int BM, int BN, int SUB, int ST, bool CONV>
-__global__ void __launch_bounds__(kThreads, 2) gemm_bf16(GemmArgs g) {
-  constexpr int kABytes = BM * kBK * 2, kBBytes = BN * kBK * 2;
-  constexpr int kSubBytes = kABytes + kBBytes;         // one 32-wide sub-slice
-  constexpr int kStageBytes = SUB * kSubBytes;
-  constexpr int kASlabs = BM / 64, kBSlabs = BN / 64;  // 1 KB DMA slabs per wave
-  constexpr int kDma = SUB * (kASlabs + kBSlabs);      // DMA instructions per stage per wave
-  constexpr int WM = BM / 2, WN = BN / 2, MB = WM / 32, NB = WN / 32;
+// One block computes a BM x BN output tile with 4 waves arranged WGM x WGN
+// (WGM * WGN = 4); each wave owns (BM/WGM) x (BN/WGN) as 32 x 32 MFMA blocks
+// computed as (W rows) x (A rows)^T, so an accumulator lane holds 4
+// consecutive output channels of one output row.  K advances BK (32 or 64) per
+// stage through an ST-stage LDS ring.
+//
+// DMA: a stage is BM A rows followed by BN W rows of BK bf16 (RB = 2*BK bytes,
+// one L2 line when BK = 64), cut into 1 KB slabs; slab s is loaded by wave
+// s % 4 with one instruction in which RB/16 consecutive lanes fetch one row.
+// When the slab count is not a multiple of 4 the first waves own one slab
+// more, and each wave waits on its own outstanding count.
+template <int BM, int BN, int WGM, int BK, int ST, int OCC, bool CONV>
+__global__ void __launch_bounds__(kThreads, OCC) gemm_bf16(GemmArgs g) {
+  constexpr int WGN = 4 / WGM;
+  constexpr int RB = BK * 2, LPR = RB / 16, RPS = 64 / LPR;  // row bytes, lanes per row, rows per slab
+  constexpr int kABytes = BM * RB;
+  constexpr int kStageBytes = (BM + BN) * RB;
+  constexpr int kASl = BM / RPS, kSl = (BM + BN) / RPS;    // slabs: A first, then W
+  constexpr int kJ = (kSl + 3) / 4;                        // slab slots per wave
+  constexpr int kRem = kSl % 4;                            // waves < kRem own kJ slabs, the rest kJ - 1
+  constexpr int kDmaHi = kJ, kDmaLo = kRem ? kJ - 1 : kJ;  // DMAs per stage per wave
+  constexpr int kQ = BK / 16;                              // 16-wide MFMA k steps per stage
+  constexpr int WM = BM / WGM, WN = BN / WGN, MB = WM / 32, NB = WN / 32;
+  static_assert(BK == 32 || BK == 64, "slice width");
+  static_assert(WGM * WGN == 4 && WM % 32 == 0 && WN % 32 == 0 && BM % RPS == 0 && BN % RPS == 0, "tile");
   __shared__ __attribute__((aligned(1024))) char lds[ST * kStageBytes];
 
   const int u = (blockIdx.x % kXcds) * g.units_per_xcd + blockIdx.x / kXcds;
   if (u >= g.units) return;
   const int tn = u % g.tiles_n, tm = u / g.tiles_n;  // tiles sharing A rows stay on one XCD
   const int m0 = tm * BM, n0 = tn * BN;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WGN, wn = wave % WGN;
   const int l32 = lane & 31, gq = lane >> 5;
+  const bool dma_hi = kRem == 0 || wave < kRem;
 
-  // ---- DMA addressing: slab j of this wave covers rows 16*(4*j + wave) + lane/4,
-  // lane l writes slot l%4 of its row, i.e. data chunk (l%4) ^ gswz(row).
   const unsigned int lds0 = __builtin_amdgcn_readfirstlane(
       static_cast<unsigned int>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)lds)) +
       wave * 1024);
-  const char* bsrc[kBSlabs];
+  const char* src[kJ];
+  int a_b[kJ], a_i[kJ], a_c[kJ], a_chunk[kJ];
+  bool has[kJ], is_a[kJ], a_ok[kJ];
 #pragma unroll
-  for (int j = 0; j < kBSlabs; ++j) {
-    const int row = 16 * (4 * j + wave) + (lane >> 2);
-    const int chunk = (lane & 3) ^ gswz(row);
-    const int n = min(n0 + row, g.N - 1);  // rows past N repeat the last one; never stored
-    const int seg = n / g.map.seg_n;
-    bsrc[j] = reinterpret_cast<const char*>(static_cast<const bf16_t*>(g.map.wts[seg]) +
-                                            static_cast<int64_t>(n - seg * g.map.seg_n) * g.K) +
-              chunk * 16;
-  }
-  const char* asrc[kASlabs];
-  int a_b[kASlabs], a_i[kASlabs], a_c[kASlabs], a_chunk[kASlabs];
-  bool a_ok[kASlabs];
-#pragma unroll
-  for (int j = 0; j < kASlabs; ++j) {
-    const int row = 16 * (4 * j + wave) + (lane >> 2);
-    a_chunk[j] = (lane & 3) ^ gswz(row);
-    const int m = m0 + row;
-    a_ok[j] = m < g.M;
-    if constexpr (CONV) {
-      const int hw = g.geo.h * g.geo.W;
-      const int mm = a_ok[j] ? m : 0;
-      a_b[j] = mm / hw;
-      const int rem = mm - a_b[j] * hw;
-      a_i[j] = rem / g.geo.W;
-      a_c[j] = rem - a_i[j] * g.geo.W;
-      asrc[j] = nullptr;
+  for (int j = 0; j < kJ; ++j) {
+    const int sl = 4 * j + wave;
+    has[j] = sl < kSl;
+    is_a[j] = sl < kASl;
+    const int row = RPS * (is_a[j] ? sl : sl - kASl) + lane / LPR;
+    const int chunk = (lane % LPR) ^ swz<BK>(row);
+    a_chunk[j] = chunk;
+    a_b[j] = a_i[j] = a_c[j] = 0;
+    a_ok[j] = false;
+    if (!is_a[j]) {
+      const int n = min(n0 + row, g.N - 1);  // rows past N repeat the last one; never stored
+      const int seg = n / g.map.seg_n;
+      src[j] = reinterpret_cast<const char*>(static_cast<const bf16_t*>(g.map.wts[seg]) +
+                                             static_cast<int64_t>(n - seg * g.map.seg_n) * g.K) +
+               chunk * 16;
     } else {
-      a_b[j] = a_i[j] = a_c[j] = 0;  // rows past M repeat the last one; never stored
-      asrc[j] = reinterpret_cast<const char*>(g.a + static_cast<int64_t>(min(m, g.M - 1)) * g.K) + a_chunk[j] * 16;
+      const int m = m0 + row;
+      a_ok[j] = m < g.M;
+      if constexpr (CONV) {
+        const int hw = g.geo.h * g.geo.W;
+        const int mm = a_ok[j] ? m : 0;
+        a_b[j] = mm / hw;
+        const int rem = mm - a_b[j] * hw;
+        a_i[j] = rem / g.geo.W;
+        a_c[j] = rem - a_i[j] * g.geo.W;
+        src[j] = nullptr;
+      } else {
+        // rows past M repeat the last one; never stored
+        src[j] = reinterpret_cast<const char*>(g.a + static_cast<int64_t>(min(m, g.M - 1)) * g.K) + chunk * 16;
+      }
     }
   }
   // conv: point the A rows at the source pixel of tap `tap` (channel 0), or the zero page
   auto conv_rows = [&](int tap) {
+    const int dy = tap / 3 - 1, dx = tap % 3 - 1;
 #pragma unroll
-    for (int j = 0; j < kASlabs; ++j) {
-      const int dy = tap / 3 - 1, dx = tap % 3 - 1;
+    for (int j = 0; j < kJ; ++j) {
+      if (!is_a[j]) continue;
       const int row = a_i[j] + dy, col = a_c[j] + dx;
-      const bf16_t* src = nullptr;
+      const bf16_t* p = nullptr;
       if (a_ok[j] && col >= 0 && col < g.geo.W) {
         if (row < 0) {
-          if (g.geo.halo_top) src = g.geo.halo_top + (static_cast<int64_t>(a_b[j]) * g.geo.W + col) * g.geo.Cin;
+          if (g.geo.halo_top) p = g.geo.halo_top + (static_cast<int64_t>(a_b[j]) * g.geo.W + col) * g.geo.Cin;
         } else if (row >= g.geo.h) {
-          if (g.geo.halo_bot) src = g.geo.halo_bot + (static_cast<int64_t>(a_b[j]) * g.geo.W + col) * g.geo.Cin;
+          if (g.geo.halo_bot) p = g.geo.halo_bot + (static_cast<int64_t>(a_b[j]) * g.geo.W + col) * g.geo.Cin;
         } else {
-          src = g.geo.x + ((static_cast<int64_t>(a_b[j]) * g.geo.h + row) * g.geo.W + col) * g.geo.Cin;
+          p = g.geo.x + ((static_cast<int64_t>(a_b[j]) * g.geo.h + row) * g.geo.W + col) * g.geo.Cin;
         }
       }
-      asrc[j] = (src ? reinterpret_cast<const char*>(src) : reinterpret_cast<const char*>(g_zero_page)) +
-                a_chunk[j] * 16;
+      src[j] = (p ? reinterpret_cast<const char*>(p) : reinterpret_cast<const char*>(g_zero_page)) +
+               a_chunk[j] * 16;
     }
   };
 
-  const int n_kt = g.K / (kBK * SUB);
-  const int kpt = CONV ? g.geo.Cin / kBK : g.K / kBK;  // 32-wide sub-slices per conv tap
-  // Issues slice kt into stage st: A slabs then B slabs; pointers advance one
-  // slice (64 bytes) per issue, and conv rows are re-pointed at each tap.
+  const int n_kt = g.K / BK;
+  const int kpt = CONV ? g.geo.Cin / BK : n_kt;  // stages per conv tap
+  // Issues the next slice into stage st; pointers advance one slice (RB bytes)
+  // per issue, and conv rows are re-pointed at each tap.
   int tap_next = 0, in_tap = 0;
   auto issue = [&](int st) {
+    if constexpr (CONV) {
+      if (in_tap == 0) conv_rows(tap_next);
+    }
 #pragma unroll
-    for (int u = 0; u < SUB; ++u) {
-      if constexpr (CONV) {
-        if (in_tap == 0) conv_rows(tap_next);
-      }
-#pragma unroll
-      for (int j = 0; j < kASlabs; ++j) {
-        gdma16(asrc[j], lds0 + st * kStageBytes + u * kSubBytes + j * 4096);
-        asrc[j] += kBK * 2;
-      }
-#pragma unroll
-      for (int j = 0; j < kBSlabs; ++j) {
-        gdma16(bsrc[j], lds0 + st * kStageBytes + u * kSubBytes + kABytes + j * 4096);
-        bsrc[j] += kBK * 2;
-      }
-      if constexpr (CONV) {
-        if (++in_tap == kpt) {
-          in_tap = 0;
-          ++tap_next;
-        }
+    for (int j = 0; j < kJ; ++j) {
+      if (!has[j]) continue;
+      gdma16(src[j], lds0 + st * kStageBytes + j * 4096);
+      src[j] += RB;
+    }
+    if constexpr (CONV) {
+      if (++in_tap == kpt) {
+        in_tap = 0;
+        ++tap_next;
       }
     }
   };
 
   // ---- operand offsets: A rows of this wave, W rows of this wave
-  int aoff[MB][2], boff[NB][2];
+  int aoff[MB][kQ], boff[NB][kQ];
 #pragma unroll
   for (int i = 0; i < MB; ++i)
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
+    for (int s = 0; s < kQ; ++s) {
       const int row = wm * WM + 32 * i + l32;
-      aoff[i][s] = row * 64 + (((2 * s + gq) ^ gswz(row)) << 4);
+      aoff[i][s] = row * RB + (((2 * s + gq) ^ swz<BK>(row)) << 4);
     }
 #pragma unroll
   for (int i = 0; i < NB; ++i)
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
+    for (int s = 0; s < kQ; ++s) {
       const int row = wn * WN + 32 * i + l32;
-      boff[i][s] = kABytes + row * 64 + (((2 * s + gq) ^ gswz(row)) << 4);
+      boff[i][s] = kABytes + row * RB + (((2 * s + gq) ^ swz<BK>(row)) << 4);
     }
 
   f32x16 acc[NB][MB];
@@ -241,27 +252,53 @@ __global__ void __launch_bounds__(kThreads, 2) gemm_bf16(GemmArgs g) {
 
   auto step = [&](auto stage_c, int kt) {
     constexpr int S = decltype(stage_c)::value;
-    if (kt + ST - 2 < n_kt) wait_vm<(ST - 2) * kDma>();  // stage kt done, later ones may be in flight
-    else wait_vm<0>();
+    if (kt + ST - 2 < n_kt) {  // stage kt done, later ones may be in flight
+      if (dma_hi) wait_vm<(ST - 2) * kDmaHi>();
+      else wait_vm<(ST - 2) * kDmaLo>();
+    } else {
+      wait_vm<0>();
+    }
     __syncthreads();  // stage kt visible; the stage of kt-1 is free
     if (kt + ST - 1 < n_kt) issue((S + ST - 1) % ST);
+    // operands of k step q+1 are read from LDS before the MFMAs of step q, so
+    // LDS latency hides behind the MFMAs
+    bf16x8 wa[2][NB], xb[2][MB];
+    auto frag = [&](int q, int b) {
 #pragma unroll
-    for (int u = 0; u < SUB; ++u)
+      for (int i = 0; i < NB; ++i)
+        wa[b][i] = *reinterpret_cast<const bf16x8*>(lds + S * kStageBytes + boff[i][q]);
 #pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        bf16x8 wa[NB], xb[MB];
+      for (int j = 0; j < MB; ++j)
+        xb[b][j] = *reinterpret_cast<const bf16x8*>(lds + S * kStageBytes + aoff[j][q]);
+    };
+    frag(0, 0);
 #pragma unroll
-        for (int i = 0; i < NB; ++i)
-          wa[i] = *reinterpret_cast<const bf16x8*>(lds + S * kStageBytes + u * kSubBytes + boff[i][s]);
+    for (int q = 0; q < kQ; ++q) {
+      if (q + 1 < kQ) frag(q + 1, (q + 1) & 1);
+#pragma unroll
+      for (int i = 0; i < NB; ++i)
 #pragma unroll
         for (int j = 0; j < MB; ++j)
-          xb[j] = *reinterpret_cast<const bf16x8*>(lds + S * kStageBytes + u * kSubBytes + aoff[j][s]);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wa[q & 1][i], xb[q & 1][j], acc[i][j], 0, 0, 0);
+    }
+    // Keep that order through instruction scheduling (which would otherwise
+    // sink each read next to its MFMA): the reads of step 0, then per step one
+    // read of the next step after each MFMA.
+    constexpr int kR = NB + MB, kP = NB * MB;
+    __builtin_amdgcn_sched_group_barrier(0x100, kR, 0);  // DS reads
 #pragma unroll
-        for (int i = 0; i < NB; ++i)
+    for (int q = 0; q < kQ; ++q) {
+      if (q + 1 < kQ) {
 #pragma unroll
-          for (int j = 0; j < MB; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wa[i], xb[j], acc[i][j], 0, 0, 0);
+        for (int t = 0; t < kP; ++t) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+          if (t < kR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        if constexpr (kR > kP) __builtin_amdgcn_sched_group_barrier(0x100, kR > kP ? kR - kP : 1, 0);
+      } else {
+        __builtin_amdgcn_sched_group_barrier(0x008, kP, 0);
       }
+    }
   };
 
 #pragma unroll
@@ -319,48 +356,60 @@ int gemm_cus() {
   return cached;
 }
 
-template <int BM, int BN, bool CONV>
+// Tile configurations: shape, wave layout, slice width and ring depth when
+// K % 64 == 0 (else 32-wide slices in a 3-stage ring), blocks per CU for the
+// launch bounds, relative time per output element (fitted to MI355X timings).
+struct TileCfg {
+  int bm, bn, wgm, bk, st, occ;
+  double cost_per_elem;
+};
+constexpr TileCfg kTiles[] = {
+    {128, 128, 2, 64, 2, 2, 1.0},   {64, 128, 2, 64, 3, 2, 1.19},  {64, 64, 2, 64, 3, 2, 1.23},
+    {160, 128, 1, 64, 2, 2, 0.875}, {96, 128, 1, 32, 3, 3, 1.07},  {128, 160, 4, 64, 2, 2, 0.94},
+};
+constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
+
+template <int C, bool CONV>
 void launch_bf16(const GemmArgs& base, hipStream_t st) {
+  constexpr TileCfg t = kTiles[C];
   GemmArgs g = base;
-  g.tiles_m = (g.M + BM - 1) / BM;
-  g.tiles_n = (g.N + BN - 1) / BN;
+  g.tiles_m = (g.M + t.bm - 1) / t.bm;
+  g.tiles_n = (g.N + t.bn - 1) / t.bn;
   g.units = g.tiles_m * g.tiles_n;
   g.units_per_xcd = (g.units + kXcds - 1) / kXcds;
   const dim3 grid(static_cast<unsigned>(g.units_per_xcd * kXcds));
-  // Two sub-slices per stage when K allows.  The 128x128 tile then runs a
-  // 2-stage ring (64 KB), so two blocks still fit a CU.
-  constexpr int ST2 = BM * BN >= 128 * 128 ? 2 : kStages;
-  if (g.K % (kSub * kBK) == 0)
-    hipLaunchKernelGGL((gemm_bf16<BM, BN, kSub, ST2, CONV>), grid, dim3(kThreads), 0, st, g);
+  if (g.K % t.bk == 0)
+    hipLaunchKernelGGL((gemm_bf16<t.bm, t.bn, t.wgm, t.bk, t.st, t.occ, CONV>), grid, dim3(kThreads), 0, st, g);
   else
-    hipLaunchKernelGGL((gemm_bf16<BM, BN, 1, kStages, CONV>), grid, dim3(kThreads), 0, st, g);
+    hipLaunchKernelGGL((gemm_bf16<t.bm, t.bn, t.wgm, kBK, kStages, t.occ, CONV>), grid, dim3(kThreads), 0, st, g);
 }
 
-// Tile shape: fewest tile-rounds per CU, weighting smaller tiles by their
-// higher cost per output element (fitted to MI355X timings of the SDXL conv
-// and projection shapes: more LDS traffic per MFMA, fewer blocks per CU).
+// Tile shape: fewest tiles per CU times tile area times the shape's cost per
+// output element.  The costs were fitted to MI355X timings of the SDXL conv,
+// projection and fused Q/K/V shapes; L2 request traffic per MFMA falls as the
+// tile grows, which is what the larger shapes buy.
 template <bool CONV>
 void launch_bf16_auto(const GemmArgs& g, hipStream_t st) {
   const int cus = gemm_cus();
-  struct Cand { int bm, bn; double cost_per_elem; };
-  const Cand cands[] = {{128, 128, 1.0}, {128, 64, 1.27}, {64, 128, 1.23}, {64, 64, 1.57}};
   int best = 0;
   double best_cost = 1e300;
-  for (int c = 0; c < 4; ++c) {
-    const int64_t tiles = static_cast<int64_t>((g.M + cands[c].bm - 1) / cands[c].bm) *
-                          ((g.N + cands[c].bn - 1) / cands[c].bn);
+  for (int c = 0; c < kNumTiles; ++c) {
+    const TileCfg& t = kTiles[c];
+    const int64_t tiles = static_cast<int64_t>((g.M + t.bm - 1) / t.bm) * ((g.N + t.bn - 1) / t.bn);
     const double per_cu = std::ceil(static_cast<double>(tiles) / cus);
-    const double cost = per_cu * cands[c].bm * cands[c].bn * cands[c].cost_per_elem;
+    const double cost = per_cu * t.bm * t.bn * t.cost_per_elem;
     if (cost < best_cost * 0.999) {
       best_cost = cost;
       best = c;
     }
   }
   switch (best) {
-    case 0: launch_bf16<128, 128, CONV>(g, st); break;
-    case 1: launch_bf16<128, 64, CONV>(g, st); break;
-    case 2: launch_bf16<64, 128, CONV>(g, st); break;
-    default: launch_bf16<64, 64, CONV>(g, st); break;
+    case 0: launch_bf16<0, CONV>(g, st); break;
+    case 1: launch_bf16<1, CONV>(g, st); break;
+    case 2: launch_bf16<2, CONV>(g, st); break;
+    case 3: launch_bf16<3, CONV>(g, st); break;
+    case 4: launch_bf16<4, CONV>(g, st); break;
+    default: launch_bf16<5, CONV>(g, st); break;
   }
 }
 

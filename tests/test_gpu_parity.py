@@ -53,6 +53,13 @@ def test_splice_bit_exact(dt, B, T_kv, C, t0, T_loc):
 @pytest.mark.parametrize("dt,M,Cin,Cout,bias", [
     ("bf16", 300, 128, 96, True), ("bf16", 1024, 640, 640, False), ("bf16", 129, 64, 32, True),
     ("bf16", 8192, 640, 640, True), ("bf16", 200, 2560, 96, False), ("bf16", 77, 32, 352, True),
+    # shapes that select each MFMA tile configuration, every one with a ragged edge
+    ("bf16", 24583, 64, 96, True),    # 128x128
+    ("bf16", 8229, 128, 96, False),   # 64x128
+    ("bf16", 16406, 160, 160, True),  # 160x128
+    ("bf16", 16406, 96, 96, False),   # 96x128, 32-wide slices
+    ("bf16", 20513, 128, 160, True),  # 128x160
+    ("bf16", 20513, 96, 160, False),  # 128x160 with 32-wide slices (K % 64 != 0)
     ("f32", 300, 64, 64, True), ("f32", 77, 50, 30, False),
 ])
 def test_linear(dt, M, Cin, Cout, bias):
@@ -69,6 +76,8 @@ def test_linear(dt, M, Cin, Cout, bias):
     ("bf16", 2, 5, 9, 64, 64, "both"), ("bf16", 1, 3, 40, 128, 96, "top"),
     ("bf16", 2, 1, 7, 64, 32, "bottom"), ("bf16", 2, 4, 33, 64, 160, "none"),
     ("bf16", 2, 3, 50, 96, 320, "both"), ("bf16", 1, 2, 200, 32, 64, "top"),
+    ("bf16", 1, 41, 400, 64, 160, "both"),   # 160x128 tiles, ragged M
+    ("bf16", 2, 13, 789, 64, 160, "bottom"), # 128x160 tiles, ragged M
     ("f32", 2, 16, 32, 64, 64, "both"), ("f32", 1, 2, 5, 6, 7, "top"),
 ])
 def test_conv3x3(dt, B, h, W, Cin, Cout, halos):
@@ -423,6 +432,7 @@ def test_stale_equals_fresh_ranks_concat_on_gpu():
 # ------------------------------------------- fused Q/K/V projection (NEXT-2)
 @pytest.mark.parametrize("dt,B,T_kv,C,t0,T_loc", [
     ("bf16", 2, 1000, 640, 300, 200), ("bf16", 1, 96, 64, 0, 96), ("bf16", 2, 333, 320, 250, 83),
+    ("bf16", 2, 8000, 640, 900, 7100),  # the 160x128 tiles of the SDXL-3840 share
     ("f32", 2, 256, 64, 64, 64), ("f32", 1, 50, 12, 40, 10),
 ])
 def test_qkv_projection_into_buffers(dt, B, T_kv, C, t0, T_loc):
