@@ -217,6 +217,57 @@ class Share:
             mark("groupnorm")
 
 
+# ------------------------------------------------------------ OTIL transmit
+def otil_timing(torch, ops, synth, steps: int):
+    """OTIL selective transmit at the pages' setting (SDXL 1024^2, 4 ranks,
+    --otil_k 32): the fp16 latent band of one rank (32 x 128 pixels, C = 4,
+    batch 2) in 8 x 8 blocks (K = 64), k = 32.  One sender step
+    (dp_otil_select_pack) and the receiver's copies from the 3 peers
+    (dp_otil_unpack), timed with HIP events on the launch stream."""
+    B, h, W, C, N, bh, bw, k = 2, 32, 128, 4, 4, 8, 8, 32
+    H, K = N * h, (h // bh) * (W // bw)
+    seq = synth.otil_latent_sequence(9, B, H, W, C, 2, bh, bw, "f16")
+    dv = lambda a: torch.from_numpy(a).cuda().to(torch.float16).contiguous()
+    band, last = dv(seq[1][:, h:2 * h]), dv(seq[0][:, h:2 * h])
+    vis = torch.ones(K, dtype=torch.uint8, device="cuda")
+    copy = dv(seq[0])
+    scores = torch.empty(K, dtype=torch.float32, device="cuda")
+    idx = torch.empty(k, dtype=torch.int32, device="cuda")
+    packed = torch.empty((k, B, bh, bw, C), dtype=torch.float16, device="cuda")
+    last0 = last.clone()
+
+    def send():
+        last.copy_(last0)  # same work every repetition: restore the last-sent state (not timed)
+        e0.record()
+        ops.dp_otil_select_pack(band, last, vis, bh, bw, k, scores=scores, idx=idx, packed=packed)
+        e1.record()
+        for p in (0, 2, 3):
+            ops.dp_otil_unpack(copy, packed, idx, p * h, h, bh, bw)
+        e2.record()
+
+    e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+    for _ in range(5):
+        send()
+    torch.cuda.synchronize()
+    ts, tu = [], []
+    for _ in range(steps):
+        send()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1) * 1e3)
+        tu.append(e1.elapsed_time(e2) * 1e3 / 3)
+    es = 2
+    band_b = B * h * W * C * es
+    blk_b = k * B * bh * bw * C * es
+    send_bytes = 2 * band_b + 3 * blk_b    # score reads x, last_sent; pack reads k blocks, writes packed + last_sent
+    unpack_bytes = 2 * blk_b               # per peer: read packed, write the blocks
+    t_s, t_u = float(np.median(ts)), float(np.median(tu))
+    return {"workload": "SDXL 1024^2 latent band 32x128, C=4, batch 2, fp16, 8x8 blocks, K=64, k=32, 4 ranks",
+            "select_pack_us": round(t_s, 2), "unpack_us_per_peer": round(t_u, 2),
+            "select_pack_bytes": send_bytes, "unpack_bytes_per_peer": unpack_bytes,
+            "select_pack_GBps": round(send_bytes / t_s / 1e3, 2),
+            "bound": "launch latency (the band is 64 KB; at 8 TB/s its bytes take 0.03 us)"}
+
+
 # -------------------------------------------------------------- CPU baseline
 def cpu_baseline(w, synth, seconds: float):
     """The oracle, as it stands, on a bounded sample of the same share; each
@@ -320,6 +371,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle's attention sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-otil", action="store_true", help="skip the OTIL selective-transmit timing")
     ap.add_argument("--qkv", choices=("fused", "separate"), default="fused",
                     help="fused: one launch projects Q/K/V and writes K/V into the buffers; "
                          "separate: three projections then the K/V splice")
@@ -411,6 +463,8 @@ def main():
         "groupnorm_GBps": kern.get("groupnorm", {}).get("GB/s"),
         "flops_counted": {k2: v2 for k2, v2 in fl.items()},
     }
+    if not args.no_otil:
+        out["otil"] = otil_timing(torch, ops, synth, 20)
     if not args.no_cpu_baseline:
         log("bench: CPU baseline (oracle on a bounded sample)")
         out["cpu_baseline"] = cpu_baseline(w, synth, args.cpu_seconds)

@@ -29,10 +29,12 @@ SIGNATURES = {
                                        I64, INT, P, SZ, P]),
     "dp_linear": (INT, [P, P, P, P, I64, I64, I64, INT, P]),
     "dp_qkv_projection_into_buffers": (INT, [P, P, P, P, P, P, P, I64, I64, I64, I64, I64, INT, P]),
+    "dp_otil_select_pack": (INT, [P, P, P, P, P, P, I64, I64, I64, I64, I64, I64, I64, F32, INT, P]),
+    "dp_otil_unpack": (INT, [P, P, P, I64, I64, I64, I64, I64, I64, I64, I64, I64, INT, P]),
 }
 
 DP_OK, DP_ERR_INVALID_ARG, DP_ERR_UNSUPPORTED, DP_ERR_HIP = 0, 1, 2, 3
-DP_F32, DP_BF16 = 0, 1
+DP_F32, DP_BF16, DP_F16 = 0, 1, 2
 
 _lib = None
 

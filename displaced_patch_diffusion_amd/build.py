@@ -19,7 +19,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libdp.so")
 
-SOURCES = ["status.cpp", "splice.hip", "groupnorm.hip", "gemm.hip", "attention.hip"]
+SOURCES = ["status.cpp", "splice.hip", "groupnorm.hip", "gemm.hip", "attention.hip", "otil.hip"]
 # Per-file extra flags.  The attention kernels take finite inputs only, so NaN
 # semantics are not kept there: fmax then maps to bare v_max3_f32 without
 # per-operand canonicalisation (infinities, used for masking, keep their meaning).

@@ -9,7 +9,7 @@ from __future__ import annotations
 
 import torch
 
-from ._lib import DP_BF16, DP_F32, check, lib
+from ._lib import DP_BF16, DP_F16, DP_F32, check, lib
 
 _DT = {torch.bfloat16: DP_BF16, torch.float32: DP_F32}
 
@@ -156,3 +156,50 @@ def dp_qkv_projection_into_buffers(x, wq, wk, wv, k_buf, v_buf, t0: int, q=None)
                                                _p(v_buf), B, T_loc, T_kv, t0, C, dt, _stream()),
           "dp_qkv_projection_into_buffers")
     return q
+
+
+_OTIL_DT = {torch.bfloat16: DP_BF16, torch.float32: DP_F32, torch.float16: DP_F16}
+
+
+def dp_otil_select_pack(x, last_sent, visited, bh: int, bw: int, k: int, bonus: float = 10.0,
+                        scores=None, idx=None, packed=None):
+    """Sender side of OTIL for the band x [B,h,W,C]: updates last_sent and
+    visited (uint8 [K]) in place; returns (scores [K] f32, idx [k] int32,
+    packed [k,B,bh,bw,C])."""
+    _dev(x, last_sent, visited, scores, idx, packed)
+    if x.dtype not in _OTIL_DT or last_sent.dtype != x.dtype or (packed is not None and packed.dtype != x.dtype):
+        raise TypeError("x, last_sent and packed must share one of f32/bf16/f16")
+    if visited.dtype != torch.uint8:
+        raise TypeError("visited must be uint8")
+    B, h, W, C = x.shape
+    if last_sent.shape != x.shape:
+        raise ValueError("last_sent must have x's shape")
+    K = (h // bh) * (W // bw) if bh > 0 and bw > 0 else 0
+    if visited.numel() != K:
+        raise ValueError(f"visited must hold {K} flags")
+    if scores is None:
+        scores = torch.empty(K, dtype=torch.float32, device=x.device)
+    if idx is None:
+        idx = torch.empty(k, dtype=torch.int32, device=x.device)
+    if packed is None:
+        packed = torch.empty((k, B, bh, bw, C), dtype=x.dtype, device=x.device)
+    if scores.dtype != torch.float32 or idx.dtype != torch.int32:
+        raise TypeError("scores must be float32 and idx int32")
+    check(lib().dp_otil_select_pack(_p(x), _p(last_sent), _p(visited), _p(scores), _p(idx), _p(packed),
+                                    B, h, W, C, bh, bw, k, bonus, _OTIL_DT[x.dtype], _stream()),
+          "dp_otil_select_pack")
+    return scores, idx, packed
+
+
+def dp_otil_unpack(dst, packed, idx, r0: int, h: int, bh: int, bw: int) -> None:
+    """Receiver side of OTIL: copies packed [k,B,bh,bw,C] blocks idx [k] into
+    rows [r0, r0+h) of dst [B,H,W,C] (in place)."""
+    _dev(dst, packed, idx)
+    if dst.dtype not in _OTIL_DT or packed.dtype != dst.dtype or idx.dtype != torch.int32:
+        raise TypeError("dst and packed must share one of f32/bf16/f16; idx must be int32")
+    B, H, W, C = dst.shape
+    k = idx.numel()
+    if packed.shape != (k, B, bh, bw, C):
+        raise ValueError("packed must be [k,B,bh,bw,C]")
+    check(lib().dp_otil_unpack(_p(dst), _p(packed), _p(idx), B, H, W, C, r0, h, bh, bw, k,
+                               _OTIL_DT[dst.dtype], _stream()), "dp_otil_unpack")

@@ -60,9 +60,11 @@ def bf16_from_bits(u: np.ndarray) -> np.ndarray:
 
 
 def as_storage(a: np.ndarray, dtype: str) -> np.ndarray:
-    """float32 array whose values are representable in ``dtype`` ('f32'|'bf16')."""
+    """float32 array whose values are representable in ``dtype`` ('f32'|'bf16'|'f16')."""
     if dtype == "bf16":
         return round_to_bf16(a)
+    if dtype == "f16":
+        return np.asarray(a, np.float32).astype(np.float16).astype(np.float32)
     if dtype == "f32":
         return np.ascontiguousarray(a, dtype=np.float32)
     raise ValueError(f"unknown dtype {dtype!r}")
@@ -275,3 +277,22 @@ def schedule_inputs(w: Workload) -> dict:
         "gamma": normal(SEED_AFFINE, "gn0.gamma", (C,), 0.1, 1.0),
         "beta": normal(SEED_AFFINE, "gn0.beta", (C,), 0.1),
     }
+
+
+def otil_latent_sequence(seed: int, B: int, H: int, W: int, C: int, steps: int, bh: int, bw: int,
+                         dtype: str) -> list:
+    """A latent [B, H, W, C] over ``steps`` denoising steps, as a random walk in
+    which each bh x bw block has its own step size: x_{s+1} = x_s + a_blk * N(0,1)
+    with the block step sizes a distinct and spread over [0.02, 1] (so the
+    blocks change by clearly different amounts).  Storage-rounded arrays."""
+    nby, nbx = H // bh, W // bw
+    amp = normal(seed, "otil.amp_order", (nby * nbx,))
+    rank = np.argsort(np.argsort(amp))  # a random permutation of the block ids
+    a = (0.02 + 0.98 * rank / max(nby * nbx - 1, 1)).astype(np.float32).reshape(nby, nbx)
+    a_full = np.repeat(np.repeat(a, bh, axis=0), bw, axis=1)[None, :, :, None]
+    x = normal(seed, "otil.x0", (B, H, W, C))
+    out = [as_storage(x, dtype)]
+    for s in range(1, steps):
+        x = out[-1] + a_full * normal(seed, f"otil.step{s}", (B, H, W, C))
+        out.append(as_storage(x, dtype))
+    return out

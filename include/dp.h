@@ -48,7 +48,9 @@ typedef enum {
   DP_ERR_HIP = 3          /* the HIP runtime reported an error at launch */
 } dp_status;
 
-typedef enum { DP_F32 = 0, DP_BF16 = 1 } dp_dtype;
+/* DP_F16 (the latent's storage type on the pages) is accepted by the OTIL calls
+ * only; every other call rejects it with DP_ERR_INVALID_ARG. */
+typedef enum { DP_F32 = 0, DP_BF16 = 1, DP_F16 = 2 } dp_dtype;
 
 /* Static description of a status code (never NULL). */
 const char* dp_status_string(dp_status s);
@@ -179,6 +181,52 @@ dp_status dp_qkv_projection_into_buffers(const void* x, const void* wq, const vo
                                          const void* wv, void* q, void* k_buf, void* v_buf,
                                          int64_t B, int64_t T_loc, int64_t T_kv, int64_t t0,
                                          int64_t C, dp_dtype dt, hipStream_t stream);
+
+/*
+ * OTIL selective block transmit, sender side: score, select and pack the
+ * blocks of the rank's latent band that its peers receive this step ("OTIL for
+ * SDXL on 4x L40S", "What is implemented where": one topk over the cosine
+ * dissimilarity plus ten times an unvisited flag, packing by index select, no
+ * host synchronisation; "Self-tests": exactly k blocks per peer).
+ * Block j is the bh x bw spatial block (row-major over the (h/bh) x (W/bw)
+ * block grid) of every batch item and channel.  Three kernels on `stream`:
+ *   scores[j] = 1 - cos(x_j, last_sent_j) + (visited[j] ? 0 : bonus),
+ *               cos = <a,b> / max(|a||b|, 1e-8), float32 accumulation;
+ *   idx[0..k) = the k blocks of highest score, highest first, equal scores in
+ *               block-id order (a NaN score ranks last);
+ *   packed[p] = block idx[p] of x; last_sent's block idx[p] = that block of x;
+ *               visited[idx[p]] = 1.
+ * x, last_sent [B, h, W, C] of dt (F32, BF16 or F16); visited [K] uint8
+ * (0/1, caller-owned state: clear it to start a new polling round); scores [K]
+ * float32 out; idx [k] int32 out; packed [k, B, bh, bw, C] of dt out;
+ * K = (h/bh)*(W/bw).  Pass bonus = 10 for the pages' rule (any value > 2 puts
+ * unvisited blocks first).
+ * Errors: INVALID_ARG for NULL pointers, sizes <= 0, h % bh or W % bw != 0,
+ * k > K, a non-finite bonus, overlapping buffers or pointers not aligned to
+ * their element size; UNSUPPORTED for K > 16384 or a band over 2 GiB.
+ */
+dp_status dp_otil_select_pack(const void* x, void* last_sent, uint8_t* visited, float* scores,
+                              int32_t* idx, void* packed, int64_t B, int64_t h, int64_t W,
+                              int64_t C, int64_t bh, int64_t bw, int64_t k, float bonus,
+                              dp_dtype dt, hipStream_t stream);
+
+/*
+ * OTIL receiver side: copies each received block into the receiver's copy of
+ * the sending peer's band, whole blocks only, so every position of that band
+ * is either a received block or the previous (stale) content, never a blend
+ * ("OTIL ...", "What is implemented where": one index copy per remote device;
+ * "Self-tests").
+ * dst [B, H, W, C] of dt, the receiver's copy of the whole latent, updated in
+ * place; the peer's band is rows [r0, r0 + h).  packed [k, B, bh, bw, C] and
+ * idx [k] int32 as produced by the peer's dp_otil_select_pack; ids outside
+ * [0, K) are skipped.
+ * Errors: INVALID_ARG for NULL pointers, sizes <= 0, r0 < 0 or r0 + h > H,
+ * h % bh or W % bw != 0, k > K, dst overlapping packed or idx, or misaligned
+ * pointers; UNSUPPORTED for a latent over 2 GiB.
+ */
+dp_status dp_otil_unpack(void* dst, const void* packed, const int32_t* idx, int64_t B, int64_t H,
+                         int64_t W, int64_t C, int64_t r0, int64_t h, int64_t bh, int64_t bw,
+                         int64_t k, dp_dtype dt, hipStream_t stream);
 
 #ifdef __cplusplus
 }

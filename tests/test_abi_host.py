@@ -143,3 +143,37 @@ def test_qkv_projection_validation(lib):
     # bf16 needs C % 32 == 0
     st, _ = status_and_error(f, A, Bp, Cp, D, E, F, H2, 2, 64, 256, 0, 48, _lib.DP_BF16, None)
     assert st == _lib.DP_ERR_UNSUPPORTED
+
+
+def test_otil_validation(lib):
+    F2, G2 = 0x60000000, 0x70000000
+    sp = lib.dp_otil_select_pack
+    ok = (A, Bp, Cp, D, E, F2, 2, 32, 128, 4, 8, 8, 32, 10.0, _lib.DP_F16, None)
+
+    def call(**kw):
+        names = ["x", "last", "vis", "scores", "idx", "packed", "B", "h", "W", "C", "bh", "bw", "k",
+                 "bonus", "dt", "st"]
+        args = dict(zip(names, ok))
+        args.update(kw)
+        return status_and_error(sp, *[args[n] for n in names])
+
+    assert call(x=None)[0] == _lib.DP_ERR_INVALID_ARG
+    assert call(h=30)[0] == _lib.DP_ERR_INVALID_ARG            # 30 % 8 != 0
+    assert call(k=65)[0] == _lib.DP_ERR_INVALID_ARG            # K = 4 * 16 = 64
+    assert call(k=0)[0] == _lib.DP_ERR_INVALID_ARG
+    assert call(bonus=float("inf"))[0] == _lib.DP_ERR_INVALID_ARG
+    assert call(dt=7)[0] == _lib.DP_ERR_INVALID_ARG
+    st, msg = call(packed=A + 64)
+    assert st == _lib.DP_ERR_INVALID_ARG and "overlap" in msg
+    assert call(x=A + 1)[0] == _lib.DP_ERR_INVALID_ARG          # misaligned f16 pointer
+    assert call(h=256, W=512, bh=1, bw=1, k=1)[0] == _lib.DP_ERR_UNSUPPORTED  # K > 16384
+    up = lib.dp_otil_unpack
+    assert status_and_error(up, A, Bp, Cp, 2, 128, 128, 4, 100, 32, 8, 8, 32, _lib.DP_F16, None)[0] == \
+        _lib.DP_ERR_INVALID_ARG                                  # rows [100, 132) outside H = 128
+    assert status_and_error(up, A, Bp, None, 2, 128, 128, 4, 0, 32, 8, 8, 32, _lib.DP_F16, None)[0] == \
+        _lib.DP_ERR_INVALID_ARG
+    assert status_and_error(up, A, A + 128, G2, 2, 128, 128, 4, 0, 32, 8, 8, 32, _lib.DP_F16, None)[0] == \
+        _lib.DP_ERR_INVALID_ARG                                  # dst overlaps packed
+    # the other calls reject F16
+    assert status_and_error(lib.dp_linear, A, Bp, None, Cp, 4, 32, 32, _lib.DP_F16, None)[0] == \
+        _lib.DP_ERR_INVALID_ARG

@@ -20,11 +20,11 @@ def gpu_ok() -> bool:
 
 
 def torch_dtype(dt: str):
-    return torch.bfloat16 if dt == "bf16" else torch.float32
+    return {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[dt]
 
 
 def dev(a: np.ndarray, dt: str) -> torch.Tensor:
-    """Exact transfer of bf16/f32-representable float32 values to the GPU."""
+    """Exact transfer of bf16/f16/f32-representable float32 values to the GPU."""
     return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda().to(torch_dtype(dt)).contiguous()
 
 
