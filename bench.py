@@ -268,6 +268,81 @@ def otil_timing(torch, ops, synth, steps: int):
             "bound": "launch latency (the band is 64 KB; at 8 TB/s its bytes take 0.03 us)"}
 
 
+# ---------------------------------------------------- row-sharded VAE decoder
+def vae_rows_timing(torch, ops, synth, name: str, steps: int):
+    """One rank's band of a KL-VAE decoder resnet in DistVAE's row mode: group
+    sums, GN+SiLU with the other bands' current sums, conv3x3 with fresh halos,
+    twice.  The neighbour bands' halos and sums are computed once beforehand;
+    only the rank's own calls are timed (HIP events on the launch stream)."""
+    from displaced_patch_diffusion_amd.vae_rows import RowShardedResnet
+    v = synth.VAE_LEVELS[name]
+    inp = synth.vae_inputs(v)
+    dt = torch.bfloat16 if v.dtype == "bf16" else torch.float32
+    dv = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).cuda().to(dt)
+    f32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).cuda()
+    wts = {}
+    for i in range(2):
+        wts[f"w{i}"] = dv(inp[f"w{i}"])
+        for k in ("b", "gamma", "beta"):
+            wts[f"{k}{i}"] = f32(inp[f"{k}{i}"])
+    net = RowShardedResnet(v.H, v.W, v.C, v.N, wts, v.G, v.eps)
+    x = dv(inp["x"])
+    B, r = v.B, v.rank
+    # the state a real run gets from its neighbours: per layer, all bands' sums
+    # and the halo rows of the normalised neighbour bands
+    xs = [x[:, a:b].contiguous() for a, b in net.bands]
+    layer = []
+    for i in range(2):
+        sums = torch.stack([ops.dp_groupnorm_sums(t.view(B, -1, v.C), v.G) for t in xs])
+        ys = net._gn(xs, i)
+        layer.append((sums, ys[r - 1][:, -1].contiguous() if r > 0 else None,
+                      ys[r + 1][:, 0].contiguous() if r + 1 < v.N else None))
+        xs = net._conv(ys, i)
+    x0 = x[:, net.bands[r][0]:net.bands[r][1]].contiguous()
+    h = x0.shape[1]
+    T = h * v.W
+    ws = torch.empty(ops.dp_groupnorm_stale_stats_workspace(B, T, v.C, v.G), dtype=torch.uint8, device="cuda")
+    y = torch.empty_like(x0)
+    z = [torch.empty_like(x0), torch.empty_like(x0)]
+    own = torch.empty((B, v.G, 2), dtype=torch.float32, device="cuda")
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(7)]
+
+    def band_step():
+        xin = x0
+        ev[0].record()
+        for i in range(2):
+            sums, top, bot = layer[i]
+            ops.dp_groupnorm_sums(xin.view(B, T, v.C), v.G, out=own, ws=ws)
+            ev[3 * i + 1].record()
+            ops.dp_groupnorm_stale_stats(xin.view(B, T, v.C), sums, r, v.H * v.W, wts[f"gamma{i}"],
+                                         wts[f"beta{i}"], v.eps, True, v.G, y=y.view(B, T, v.C), ws=ws)
+            ev[3 * i + 2].record()
+            ops.dp_conv3x3_stale_halo(y, top, bot, wts[f"w{i}"], wts[f"b{i}"], y=z[i])
+            ev[3 * i + 3].record()
+            xin = z[i]
+
+    for _ in range(3):
+        band_step()
+    torch.cuda.synchronize()
+    acc = {"sums": [], "gn": [], "conv": []}
+    for _ in range(steps):
+        band_step()
+        torch.cuda.synchronize()
+        for i in range(2):
+            acc["sums"].append(ev[3 * i].elapsed_time(ev[3 * i + 1]) * 1e3)
+            acc["gn"].append(ev[3 * i + 1].elapsed_time(ev[3 * i + 2]) * 1e3)
+            acc["conv"].append(ev[3 * i + 2].elapsed_time(ev[3 * i + 3]) * 1e3)
+    med = {k: float(np.median(a)) for k, a in acc.items()}
+    fl, gb = v.conv_flops(), v.gn_bytes()
+    return {"workload": f"{v.name}: {v.note}; band {h}x{v.W}x{v.C}, batch {B}, rank {r} of {v.N}",
+            "conv_us": round(med["conv"], 2), "conv_TFLOPs": round(fl / med["conv"] / 1e6, 1),
+            "conv_frac": round(fl / med["conv"] / 1e6 / PEAK_BF16_TFLOPS, 4),
+            "groupnorm_sums_us": round(med["sums"], 2), "groupnorm_apply_us": round(med["gn"], 2),
+            "groupnorm_GBps": round(gb / (med["sums"] + med["gn"]) / 1e3, 1),
+            "groupnorm_frac": round(gb / (med["sums"] + med["gn"]) / 1e3 / PEAK_HBM_GBPS, 4),
+            "resnet_us": round(2 * (med["sums"] + med["gn"] + med["conv"]), 2)}
+
+
 # -------------------------------------------------------------- CPU baseline
 def cpu_baseline(w, synth, seconds: float):
     """The oracle, as it stands, on a bounded sample of the same share; each
@@ -372,6 +447,7 @@ def main():
                     help="target CPU time of the oracle's attention sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-otil", action="store_true", help="skip the OTIL selective-transmit timing")
+    ap.add_argument("--no-vae", action="store_true", help="skip the row-sharded VAE decoder timing")
     ap.add_argument("--qkv", choices=("fused", "separate"), default="fused",
                     help="fused: one launch projects Q/K/V and writes K/V into the buffers; "
                          "separate: three projections then the K/V splice")
@@ -465,6 +541,9 @@ def main():
     }
     if not args.no_otil:
         out["otil"] = otil_timing(torch, ops, synth, 20)
+    if not args.no_vae:
+        out["vae_rows"] = [vae_rows_timing(torch, ops, synth, n, 10)
+                           for n in ("vae_kl1024_l1024_c128", "vae_kl2048_l2048_c128")]
     if not args.no_cpu_baseline:
         log("bench: CPU baseline (oracle on a bounded sample)")
         out["cpu_baseline"] = cpu_baseline(w, synth, args.cpu_seconds)

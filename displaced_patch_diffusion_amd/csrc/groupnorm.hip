@@ -172,6 +172,26 @@ __device__ void block_group_sums(const float* s1, const float* s2, bool active, 
   __syncthreads();
 }
 
+// Folds the tile partials of batch item b into lane sums red[q*G + g] (lane q
+// takes tiles q, q + lanes, ...); returns the lane count.  One fixed order, so
+// every block (and dp_groupnorm_sums) derives bit-identical sums.
+__device__ int fold_partials(const GnArgs& a, int b, float2* red) {
+  const int G = a.G;
+  const int lanes = G >= kThreads ? 1 : kThreads / G;
+  const float2* pb = a.partial + static_cast<int64_t>(b) * a.tiles * G;
+  for (int f = threadIdx.x; f < lanes * G; f += kThreads) {
+    const int g = f % G, q = f / G;
+    float2 s = make_float2(0.f, 0.f);
+    for (int t = q; t < a.tiles; t += lanes) {
+      const float2 p = pb[static_cast<int64_t>(t) * G + g];
+      s.x += p.x;
+      s.y += p.y;
+    }
+    red[f] = s;
+  }
+  return lanes;
+}
+
 // Statistics of batch item b from the lane sums red[q*G + g] (lanes in
 // order): fresh local sums out (tile 0 only), stale sums of the other
 // patches added, (mean, rstd) per group into gstat.
@@ -283,18 +303,7 @@ __global__ void __launch_bounds__(kThreads) gn_apply(GnArgs a) {
   for (int u = 0; u < kUnroll; ++u)
     first[u] = load_or_zero<BF16>(a, b, t_begin + tl + u * tpp, t_end, vi, active && u < npass);
 
-  const int lanes = G >= kThreads ? 1 : kThreads / G;
-  const float2* pb = a.partial + static_cast<int64_t>(b) * a.tiles * G;
-  for (int f = tid; f < lanes * G; f += kThreads) {
-    const int g = f % G, q = f / G;
-    float2 s = make_float2(0.f, 0.f);
-    for (int t = q; t < a.tiles; t += lanes) {
-      const float2 p = pb[static_cast<int64_t>(t) * G + g];
-      s.x += p.x;
-      s.y += p.y;
-    }
-    red[f] = s;
-  }
+  const int lanes = fold_partials(a, b, red);
   __syncthreads();
   finalize_stats(a, b, tile, lanes, red, gstat);
   __syncthreads();
@@ -313,6 +322,24 @@ __global__ void __launch_bounds__(kThreads) gn_apply(GnArgs a) {
       const int t = t_begin + tl + (k0 + u) * tpp;
       if (k0 + u < npass && t < t_end) normalize_store<BF16>(a, b, t, vi, raw[u], ca, cb);
     }
+  }
+}
+
+// Local sums only: one block per batch item folds the partials (in the order
+// gn_apply uses) and writes (sum x, sum x^2) per group.
+__global__ void __launch_bounds__(kThreads) gn_sums(GnArgs a) {
+  __shared__ float2 red[2048];
+  const int b = blockIdx.y, G = a.G;
+  const int lanes = fold_partials(a, b, red);
+  __syncthreads();
+  for (int g = threadIdx.x; g < G; g += kThreads) {
+    float f1 = 0.f, f2 = 0.f;
+    for (int q = 0; q < lanes; ++q) {
+      f1 += red[q * G + g].x;
+      f2 += red[q * G + g].y;
+    }
+    a.fresh[(static_cast<int64_t>(b) * G + g) * 2 + 0] = f1;
+    a.fresh[(static_cast<int64_t>(b) * G + g) * 2 + 1] = f2;
   }
 }
 
@@ -410,4 +437,40 @@ DP_API dp_status dp_groupnorm_stale_stats(const void* x, const float* stale_sums
     hipLaunchKernelGGL(gn_apply<false>, grid, dim3(kThreads), 0, stream, ga);
   }
   return dp::check_launch("dp_groupnorm_stale_stats");
+}
+
+DP_API dp_status dp_groupnorm_sums(const void* x, float* sums_out, int64_t B, int64_t T_loc, int64_t C, int64_t G,
+                                   dp_dtype dt, void* ws, size_t ws_bytes, hipStream_t stream) {
+  using dp::fail;
+  const char* name = "dp_groupnorm_sums";
+  if (!x || !sums_out) return fail(DP_ERR_INVALID_ARG, "%s: NULL x or sums_out", name);
+  if (B <= 0 || T_loc <= 0 || C <= 0 || G <= 0) return fail(DP_ERR_INVALID_ARG, "%s: sizes must be positive", name);
+  if (C % G != 0) return fail(DP_ERR_INVALID_ARG, "%s: C %% G != 0", name);
+  if (!dp::dtype_ok(dt)) return fail(DP_ERR_INVALID_ARG, "%s: bad dtype", name);
+  const size_t need = workspace_bytes(B, T_loc, G);
+  if (!ws || ws_bytes < need) return fail(DP_ERR_INVALID_ARG, "%s: workspace %zu < %zu bytes", name, ws_bytes, need);
+  const int vec = dt == DP_BF16 ? 8 : 4;
+  if (C % vec != 0 || C > 2048 || C / vec > kThreads || T_loc > 0x7FFFFFFF || B > 65535 || B * G > 0x7FFFFFFF)
+    return fail(DP_ERR_UNSUPPORTED, "%s: C=%lld G=%lld not supported", name, (long long)C, (long long)G);
+  const size_t xb = static_cast<size_t>(B * T_loc * C) * dp::dtype_size(dt);
+  if (dp::overlaps(x, xb, sums_out, static_cast<size_t>(B * G) * 8) || dp::overlaps(ws, need, sums_out, static_cast<size_t>(B * G) * 8))
+    return fail(DP_ERR_INVALID_ARG, "%s: sums_out overlaps x or the workspace", name);
+  const GnPlan p = make_plan(B, T_loc, C, dt);
+  GnArgs ga{};
+  ga.x = x;
+  ga.partial = static_cast<float2*>(ws);
+  ga.fresh = sums_out;
+  ga.T = static_cast<int>(T_loc);
+  ga.C = static_cast<int>(C);
+  ga.G = static_cast<int>(G);
+  ga.tiles = p.tiles;
+  ga.tile_tokens = p.tile_tokens;
+  ga.n_patches = 1;
+  ga.B = static_cast<int>(B);
+  dp::clear_error();
+  const dim3 grid(static_cast<unsigned>(p.tiles), static_cast<unsigned>(B));
+  if (dt == DP_BF16) hipLaunchKernelGGL(gn_partial<true>, grid, dim3(kThreads), 0, stream, ga);
+  else hipLaunchKernelGGL(gn_partial<false>, grid, dim3(kThreads), 0, stream, ga);
+  hipLaunchKernelGGL(gn_sums, dim3(1, static_cast<unsigned>(B)), dim3(kThreads), 0, stream, ga);
+  return dp::check_launch(name);
 }

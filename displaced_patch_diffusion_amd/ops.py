@@ -125,6 +125,20 @@ def dp_groupnorm_stale_stats(x, stale_sums, rank: int, T_total: int, gamma=None,
     return y
 
 
+def dp_groupnorm_sums(x, G: int = 32, out=None, ws=None):
+    """x [B,T_loc,C] -> (sum x, sum x^2) per group, [B,G,2] float32."""
+    _dev(x, out, ws)
+    dt = _dt(x)
+    B, T_loc, C = x.shape
+    if out is None:
+        out = torch.empty((B, G, 2), dtype=torch.float32, device=x.device)
+    if ws is None:
+        ws = _ws(lib().dp_groupnorm_stale_stats_workspace(B, T_loc, C, G), x.device)
+    check(lib().dp_groupnorm_sums(_p(x), _p(out), B, T_loc, C, G, dt, _p(ws),
+                                  0 if ws is None else ws.numel(), _stream()), "dp_groupnorm_sums")
+    return out
+
+
 def dp_linear(x, w, bias=None, y=None):
     """x [..., Cin], w [Cout, Cin] -> y [..., Cout]."""
     _dev(x, w, y, f32=(bias,))

@@ -296,3 +296,68 @@ def otil_latent_sequence(seed: int, B: int, H: int, W: int, C: int, steps: int, 
         x = out[-1] + a_full * normal(seed, f"otil.step{s}", (B, H, W, C))
         out.append(as_storage(x, dtype))
     return out
+
+
+# ------------------------------------------------------ row-sharded VAE decoder
+@dataclass(frozen=True)
+class VaeLevel:
+    """One resnet of a KL-VAE decoder level, row-sharded over N ranks:
+    GN+SiLU -> conv3x3 -> GN+SiLU -> conv3x3 on a [B, H, W, C] activation, with
+    fresh halos and GroupNorm statistics over the whole image."""
+    name: str
+    dtype: str
+    B: int
+    H: int
+    W: int
+    C: int
+    N: int
+    rank: int
+    G: int = 32
+    eps: float = 1e-5
+    note: str = field(default="", compare=False)
+
+    def rows(self, r: int | None = None) -> tuple[int, int]:
+        r = self.rank if r is None else r
+        return (r * self.H) // self.N, ((r + 1) * self.H) // self.N
+
+    @property
+    def h(self) -> int:
+        r0, r1 = self.rows()
+        return r1 - r0
+
+    def conv_flops(self) -> int:
+        """One conv of the rank's band (all nine taps counted)."""
+        return 2 * self.B * self.h * self.W * self.C * 9 * self.C
+
+    def gn_bytes(self) -> int:
+        """One GroupNorm of the rank's band: read x, write y."""
+        return 2 * self.B * self.h * self.W * self.C * (4 if self.dtype == "f32" else 2)
+
+
+# The KL VAE decoder's widest levels at the pages' canonical sizes (the kl
+# family's 1024x1024 and 2048x2048, 4 ranks): 128 channels at full resolution
+# and 256 channels at half resolution.
+VAE_LEVELS: dict[str, VaeLevel] = {
+    "vae_kl1024_l1024_c128": VaeLevel("vae_kl1024_l1024_c128", "bf16", 1, 1024, 1024, 128, 4, 1,
+                                      note="KL decoder, 1024^2 output, last level (128 ch), 4 ranks"),
+    "vae_kl1024_l512_c256": VaeLevel("vae_kl1024_l512_c256", "bf16", 1, 512, 512, 256, 4, 1,
+                                     note="KL decoder, 1024^2 output, 512^2 level (256 ch), 4 ranks"),
+    "vae_kl2048_l2048_c128": VaeLevel("vae_kl2048_l2048_c128", "bf16", 1, 2048, 2048, 128, 4, 1,
+                                      note="KL decoder, 2048^2 output, last level (128 ch), 4 ranks"),
+    "vae_small_fp32": VaeLevel("vae_small_fp32", "f32", 2, 32, 24, 64, 4, 1,
+                               note="small fp32 case the oracle runs in seconds"),
+}
+
+
+def vae_inputs(v: VaeLevel) -> dict:
+    """Whole-image activation and the resnet's weights: weights seed 0,
+    activation seed 1 (as the DistVAE bench builds its synthetic model)."""
+    B, H, W, C, dt = v.B, v.H, v.W, v.C, v.dtype
+    out = {"x": as_storage(normal(SEED_ACTIVATIONS, f"{v.name}.x", (B, H, W, C)), dt)}
+    for i in range(2):
+        out[f"w{i}"] = as_storage(normal(SEED_WEIGHTS, f"{v.name}.conv{i}.w", (C, 3, 3, C),
+                                         1.0 / np.sqrt(9 * C)), dt)
+        out[f"b{i}"] = normal(SEED_AFFINE, f"{v.name}.conv{i}.b", (C,), 0.1)
+        out[f"gamma{i}"] = normal(SEED_AFFINE, f"{v.name}.gn{i}.gamma", (C,), 0.1, 1.0)
+        out[f"beta{i}"] = normal(SEED_AFFINE, f"{v.name}.gn{i}.beta", (C,), 0.1)
+    return out

@@ -1,0 +1,56 @@
+"""Row-sharded VAE decoder resnet on one GPU (DistVAE row mode).
+
+"Benchmarking DistVAE", "Default suite", item 2: adapted layers process
+rank-local row bands, exchange halos and reassemble the output; "Glossary":
+a halo is the neighbouring rows a sharded convolution needs.  Unlike the
+displaced diffusion step, everything here is fresh: each conv takes its halo
+rows from the neighbouring bands' current output, and each GroupNorm combines
+the rank's own sums with the other bands' current sums (dp_groupnorm_sums).
+
+One resnet = GN+SiLU -> conv3x3 -> GN+SiLU -> conv3x3.  Every step runs in
+libdp; this module only orders the calls and slices the bands.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import ops
+
+
+class RowShardedResnet:
+    """weights: torch tensors w0, w1 [C,3,3,C], b0, b1 [C] f32, gamma0/1, beta0/1 [C] f32."""
+
+    def __init__(self, H: int, W: int, C: int, N: int, weights: dict, G: int = 32, eps: float = 1e-5):
+        self.H, self.W, self.C, self.N, self.G, self.eps = H, W, C, N, G, eps
+        self.wt = weights
+        self.bands = [((r * H) // N, ((r + 1) * H) // N) for r in range(N)]
+
+    def _gn(self, xs: list, i: int) -> list:
+        """GroupNorm+SiLU of every band with whole-image statistics."""
+        B = xs[0].shape[0]
+        sums = torch.stack([ops.dp_groupnorm_sums(x.view(B, -1, self.C), self.G) for x in xs])
+        out = []
+        for r, x in enumerate(xs):
+            out.append(ops.dp_groupnorm_stale_stats(
+                x.view(B, -1, self.C), sums, r, self.H * self.W, self.wt[f"gamma{i}"], self.wt[f"beta{i}"],
+                self.eps, True, self.G).view_as(x))
+        return out
+
+    def _conv(self, ys: list, i: int) -> list:
+        """conv3x3 of every band with fresh halo rows from its neighbours."""
+        out = []
+        for r, y in enumerate(ys):
+            top = ys[r - 1][:, -1].contiguous() if r > 0 else None
+            bot = ys[r + 1][:, 0].contiguous() if r + 1 < self.N else None
+            out.append(ops.dp_conv3x3_stale_halo(y, top, bot, self.wt[f"w{i}"], self.wt[f"b{i}"]))
+        return out
+
+    def forward_bands(self, x_full: torch.Tensor) -> list:
+        """x_full [B,H,W,C] -> the output bands [B,h_r,W,C]."""
+        xs = [x_full[:, a:b].contiguous() for a, b in self.bands]
+        for i in range(2):
+            xs = self._conv(self._gn(xs, i), i)
+        return xs
+
+    def forward(self, x_full: torch.Tensor) -> torch.Tensor:
+        return torch.cat(self.forward_bands(x_full), dim=1)

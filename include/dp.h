@@ -148,6 +148,24 @@ dp_status dp_groupnorm_stale_stats(const void* x, const float* stale_sums, int64
                                    hipStream_t stream);
 
 /*
+ * Local GroupNorm sums only: the first half of a GroupNorm whose statistics
+ * are combined across row bands before normalising (DistVAE row mode,
+ * "Benchmarking DistVAE", "Default suite", item 2: adapted layers work on
+ * rank-local row bands; "OTIL ...", "What is implemented where": the two
+ * scalars per group are what ranks exchange).  The sums are bit-identical to
+ * the fresh_sums_out dp_groupnorm_stale_stats writes for the same x.
+ *   sums_out[b, g, :] = (sum x, sum x^2) over the T_loc tokens and the C/G
+ *   channels of group g, float32.
+ * x [B, T_loc, C] of dt; sums_out [B, G, 2] float32; ws/ws_bytes as for
+ * dp_groupnorm_stale_stats (dp_groupnorm_stale_stats_workspace).
+ * Supported and errors: as dp_groupnorm_stale_stats (C % G == 0, C % 8 == 0 for
+ * bf16 or C % 4 == 0 for f32, C <= 2048); INVALID_ARG also when sums_out
+ * overlaps x or the workspace.
+ */
+dp_status dp_groupnorm_sums(const void* x, float* sums_out, int64_t B, int64_t T_loc, int64_t C,
+                            int64_t G, dp_dtype dt, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
  * Dense projection of the rank's own rows (the Q/K/V and output projections
  * inside the displaced self-attention layer; only local rows are projected,
  * stale rows are never recomputed):
