@@ -49,6 +49,7 @@ class Share:
     """Device tensors of one rank's share plus its stale state."""
 
     fused_qkv = True
+    gn_sums_in_conv = False
 
     def __init__(self, w, torch, ops, synth):
         self.w, self.torch, self.ops = w, torch, ops
@@ -169,6 +170,8 @@ class Share:
         self.zc = [mk(B, Tc, Cc) for _ in range(2)]
         self.gc = [mk(B, Tc, Cc) for _ in range(2)]
         self.fresh = [torch.empty((B, G, 2), dtype=torch.float32, device="cuda") for _ in range(2)]
+        self.conv_ws = torch.empty(ops.dp_conv3x3_gn_sums_workspace(B, hc, Wc, Cc), dtype=torch.uint8,
+                                   device="cuda")
         if not w.two_level:
             self.conv_in_loc = None
         torch.cuda.synchronize()
@@ -182,12 +185,22 @@ class Share:
             x = self.conv_in_loc
             for i in range(2):
                 gi, ci = self.gns[i], self.convs[i]
-                ops.dp_groupnorm_stale_stats(x, gi["stale"], w.rank, w.conv_H * Wc, gi["gamma"],
-                                             gi["beta"], w.eps, True, self.G, y=self.gc[i],
-                                             fresh_sums_out=self.fresh[i], ws=self.gn_ws)
+                if self.gn_sums_in_conv and i == 1:
+                    ops.dp_groupnorm_apply(x, self.fresh[1], gi["stale"], w.rank, w.conv_H * Wc, gi["gamma"],
+                                           gi["beta"], w.eps, True, self.G, y=self.gc[i])
+                else:
+                    ops.dp_groupnorm_stale_stats(x, gi["stale"], w.rank, w.conv_H * Wc, gi["gamma"],
+                                                 gi["beta"], w.eps, True, self.G, y=self.gc[i],
+                                                 fresh_sums_out=self.fresh[i], ws=self.gn_ws)
                 mark("groupnorm")
-                ops.dp_conv3x3_stale_halo(self.gc[i].view(B, hc, Wc, Cc), ci["ht"], ci["hb"], ci["w"],
-                                          ci["b"], y=self.zc[i].view(B, hc, Wc, Cc))
+                if self.gn_sums_in_conv and i == 0:
+                    # the conv epilogue also forms the local sums the next GroupNorm needs
+                    ops.dp_conv3x3_stale_halo_gn_sums(self.gc[i].view(B, hc, Wc, Cc), ci["ht"], ci["hb"],
+                                                      ci["w"], ci["b"], self.G, y=self.zc[i].view(B, hc, Wc, Cc),
+                                                      gn_sums=self.fresh[1], ws=self.conv_ws)
+                else:
+                    ops.dp_conv3x3_stale_halo(self.gc[i].view(B, hc, Wc, Cc), ci["ht"], ci["hb"], ci["w"],
+                                              ci["b"], y=self.zc[i].view(B, hc, Wc, Cc))
                 mark("conv")
                 x = self.zc[i]
         if self.fused_qkv:
@@ -208,12 +221,20 @@ class Share:
         mark("proj")
         if not w.two_level:
             c, g = self.convs[0], self.gns[0]
-            ops.dp_conv3x3_stale_halo(self.y.view(B, self.hc, w.conv_W, w.conv_C), c["ht"], c["hb"],
-                                      c["w"], c["b"], y=self.zc[0].view(B, self.hc, w.conv_W, w.conv_C))
-            mark("conv")
-            ops.dp_groupnorm_stale_stats(self.zc[0], g["stale"], w.rank, w.conv_H * w.conv_W,
-                                         g["gamma"], g["beta"], w.eps, False, self.G, y=self.gc[0],
-                                         fresh_sums_out=self.fresh[0], ws=self.gn_ws)
+            shp = (B, self.hc, w.conv_W, w.conv_C)
+            if self.gn_sums_in_conv:
+                # the conv epilogue forms the GroupNorm's local sums; the GroupNorm is one pass
+                ops.dp_conv3x3_stale_halo_gn_sums(self.y.view(shp), c["ht"], c["hb"], c["w"], c["b"], self.G,
+                                                  y=self.zc[0].view(shp), gn_sums=self.fresh[0], ws=self.conv_ws)
+                mark("conv")
+                ops.dp_groupnorm_apply(self.zc[0], self.fresh[0], g["stale"], w.rank, w.conv_H * w.conv_W,
+                                       g["gamma"], g["beta"], w.eps, False, self.G, y=self.gc[0])
+            else:
+                ops.dp_conv3x3_stale_halo(self.y.view(shp), c["ht"], c["hb"], c["w"], c["b"], y=self.zc[0].view(shp))
+                mark("conv")
+                ops.dp_groupnorm_stale_stats(self.zc[0], g["stale"], w.rank, w.conv_H * w.conv_W,
+                                             g["gamma"], g["beta"], w.eps, False, self.G, y=self.gc[0],
+                                             fresh_sums_out=self.fresh[0], ws=self.gn_ws)
             mark("groupnorm")
 
 
@@ -446,6 +467,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle's attention sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--gn-sums", choices=("conv", "separate"), default="separate",
+                    help="conv: the conv epilogue forms the GroupNorm's local sums and the GroupNorm is one "
+                         "pass; separate: the GroupNorm forms them in a read pass of its own")
     ap.add_argument("--no-otil", action="store_true", help="skip the OTIL selective-transmit timing")
     ap.add_argument("--no-vae", action="store_true", help="skip the row-sharded VAE decoder timing")
     ap.add_argument("--qkv", choices=("fused", "separate"), default="fused",
@@ -470,6 +494,7 @@ def main():
     log(f"bench: workload {w.name}: building inputs")
     share = Share(w, torch, ops, synth)
     share.fused_qkv = args.qkv == "fused"
+    share.gn_sums_in_conv = args.gn_sums == "conv"
 
     names = []
 
@@ -532,7 +557,7 @@ def main():
         "config": {"workload": w.name, "batch": w.B, "attn_level": f"{w.attn_H}x{w.attn_W}",
                    "C_attn": w.attn_C, "heads": w.heads, "head_dim": w.head_dim,
                    "conv_level": f"{w.conv_H}x{w.conv_W}", "C_conv": w.conv_C, "n_patches": w.N,
-                   "rank": w.rank, "Tq": w.Tq, "T_kv": w.T_kv, "qkv": args.qkv,
+                   "rank": w.rank, "Tq": w.Tq, "T_kv": w.T_kv, "qkv": args.qkv, "gn_sums": args.gn_sums,
                    "parallelism": "one rank's share, 1 GPU"},
         "roofline": roofline,
         "kernels": kern,

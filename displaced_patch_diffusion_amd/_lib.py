@@ -28,6 +28,9 @@ SIGNATURES = {
     "dp_groupnorm_stale_stats": (INT, [P, P, I64, I64, I64, P, P, F32, INT, P, P, I64, I64, I64,
                                        I64, INT, P, SZ, P]),
     "dp_groupnorm_sums": (INT, [P, P, I64, I64, I64, I64, INT, P, SZ, P]),
+    "dp_groupnorm_apply": (INT, [P, P, P, I64, I64, I64, P, P, F32, INT, P, I64, I64, I64, I64, INT, P]),
+    "dp_conv3x3_gn_sums_workspace": (SZ, [I64, I64, I64, I64]),
+    "dp_conv3x3_stale_halo_gn_sums": (INT, [P, P, P, P, P, P, P, I64, P, SZ, I64, I64, I64, I64, I64, INT, P]),
     "dp_linear": (INT, [P, P, P, P, I64, I64, I64, INT, P]),
     "dp_qkv_projection_into_buffers": (INT, [P, P, P, P, P, P, P, I64, I64, I64, I64, I64, INT, P]),
     "dp_otil_select_pack": (INT, [P, P, P, P, P, P, I64, I64, I64, I64, I64, I64, I64, F32, INT, P]),

@@ -69,6 +69,8 @@ struct GemmArgs {
   const float* bias;   // [N] or null
   int M, N, K;
   int tiles_m, tiles_n, units, units_per_xcd;
+  float2* gpart;       // GroupNorm partials [tiles_m * WGM][2][N] (conv with sums only)
+  int gT;              // output tokens per batch item (conv with sums only)
 };
 
 // LDS rows of 64 bytes (BK = 32) or 128 bytes (BK = 64): 16-byte chunk c of
@@ -115,7 +117,7 @@ struct Stage {
 // s % 4 with one instruction in which RB/16 consecutive lanes fetch one row.
 // When the slab count is not a multiple of 4 the first waves own one slab
 // more, and each wave waits on its own outstanding count.
-template <int BM, int BN, int WGM, int BK, int ST, int OCC, bool CONV>
+template <int BM, int BN, int WGM, int BK, int ST, int OCC, bool CONV, bool GNS = false>
 __global__ void __launch_bounds__(kThreads, OCC) gemm_bf16(GemmArgs g) {
   constexpr int WGN = 4 / WGM;
   constexpr int RB = BK * 2, LPR = RB / 16, RPS = 64 / LPR;  // row bytes, lanes per row, rows per slab
@@ -336,6 +338,89 @@ __global__ void __launch_bounds__(kThreads, OCC) gemm_bf16(GemmArgs g) {
         *reinterpret_cast<u32x2*>(yrow + n) = packed;
       }
     }
+
+  if constexpr (GNS) {
+    // GroupNorm partials of the stored (bf16-rounded) outputs: per channel,
+    // (sum y, sum y^2) over this wave's rows of the batch item of the tile's
+    // first row (segment 0) and of the next one (segment 1; a tile spans at
+    // most two since gT >= BM).  Rows are summed in-lane over the row blocks,
+    // then across the 32 lanes of each half-wave by a fixed butterfly, so the
+    // result does not depend on scheduling.
+    const int mw0 = m0 + wm * WM;
+    const int b0 = m0 / g.gT;
+    const int nseg = (min(m0 + BM, g.M) - 1) / g.gT - b0 + 1;
+    float2* prow = g.gpart + (static_cast<int64_t>(tm) * WGM + wm) * 2 * g.N;
+    for (int sg = 0; sg < nseg; ++sg) {
+#pragma unroll
+      for (int i = 0; i < NB; ++i) {
+        const int nblk = n0 + wn * WN + 32 * i;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {  // channels nblk + 8q + 4gq + (0..3)
+          float s1[4] = {0.f, 0.f, 0.f, 0.f}, s2[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int j = 0; j < MB; ++j) {
+            const int m = mw0 + 32 * j + l32;
+            const bool on = m < g.M && m / g.gT - b0 == sg && nblk < g.N;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int n = min(nblk + 8 * q + 4 * gq + e, g.N - 1);
+              const float v =
+                  static_cast<float>(static_cast<__bf16>(acc[i][j][4 * q + e] + (g.bias ? g.bias[n] : 0.f)));
+              s1[e] += on ? v : 0.f;
+              s2[e] += on ? v * v : 0.f;
+            }
+          }
+#pragma unroll
+          for (int off = 1; off < 32; off <<= 1)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              s1[e] += __shfl_xor(s1[e], off, 64);
+              s2[e] += __shfl_xor(s2[e], off, 64);
+            }
+          if (l32 == 0 && nblk < g.N) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) prow[sg * g.N + nblk + 8 * q + 4 * gq + e] = make_float2(s1[e], s2[e]);
+          }
+        }
+      }
+    }
+  }
+}
+
+// Folds the conv epilogue's GroupNorm partials into (sum, sum of squares) per
+// (batch item, group): one block per (group, batch item).  The partials of
+// the item's tiles (tiles in order, then wave row groups, then the group's
+// channels) are dealt to the threads round-robin, summed in order per thread,
+// then combined by a fixed tree: deterministic.
+constexpr int kFoldThreads = 256;
+__global__ void __launch_bounds__(kFoldThreads)
+gn_conv_fold(const float2* __restrict__ gpart, float* __restrict__ out, int N, int G, int gT, int BM, int WGM) {
+  __shared__ float2 red[kFoldThreads];
+  const int gi = blockIdx.x, b = blockIdx.y, Cg = N / G;
+  const int tm_lo = (b * gT) / BM, tm_hi = ((b + 1) * gT - 1) / BM;
+  const int total = (tm_hi - tm_lo + 1) * WGM * Cg;
+  float2 acc = make_float2(0.f, 0.f);
+  for (int e = threadIdx.x; e < total; e += kFoldThreads) {
+    const int c = e % Cg, r = e / Cg;
+    const int w = r % WGM, tm = tm_lo + r / WGM;
+    const int sg = b - (tm * BM) / gT;
+    const float2 p = gpart[(static_cast<int64_t>(tm) * WGM + w) * 2 * N + sg * N + gi * Cg + c];
+    acc.x += p.x;
+    acc.y += p.y;
+  }
+  red[threadIdx.x] = acc;
+  __syncthreads();
+  for (int half = kFoldThreads / 2; half > 0; half >>= 1) {
+    if (threadIdx.x < half) {
+      red[threadIdx.x].x += red[threadIdx.x + half].x;
+      red[threadIdx.x].y += red[threadIdx.x + half].y;
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    out[(static_cast<int64_t>(b) * G + gi) * 2 + 0] = red[0].x;
+    out[(static_cast<int64_t>(b) * G + gi) * 2 + 1] = red[0].y;
+  }
 }
 
 int gemm_cus() {
@@ -384,12 +469,30 @@ void launch_bf16(const GemmArgs& base, hipStream_t st) {
     hipLaunchKernelGGL((gemm_bf16<t.bm, t.bn, t.wgm, kBK, kStages, t.occ, CONV>), grid, dim3(kThreads), 0, st, g);
 }
 
+// Conv with GroupNorm partials: same tile choice, GNS epilogue, then the fold.
+template <int C>
+void launch_bf16_gns(const GemmArgs& base, float* sums, int G, hipStream_t st) {
+  constexpr TileCfg t = kTiles[C];
+  GemmArgs g = base;
+  g.tiles_m = (g.M + t.bm - 1) / t.bm;
+  g.tiles_n = (g.N + t.bn - 1) / t.bn;
+  g.units = g.tiles_m * g.tiles_n;
+  g.units_per_xcd = (g.units + kXcds - 1) / kXcds;
+  const dim3 grid(static_cast<unsigned>(g.units_per_xcd * kXcds));
+  if (g.K % t.bk == 0)
+    hipLaunchKernelGGL((gemm_bf16<t.bm, t.bn, t.wgm, t.bk, t.st, t.occ, true, true>), grid, dim3(kThreads), 0, st, g);
+  else
+    hipLaunchKernelGGL((gemm_bf16<t.bm, t.bn, t.wgm, kBK, kStages, t.occ, true, true>), grid, dim3(kThreads), 0, st, g);
+  const int B = g.M / g.gT;
+  hipLaunchKernelGGL(gn_conv_fold, dim3(static_cast<unsigned>(G), static_cast<unsigned>(B)), dim3(kFoldThreads), 0, st,
+                     g.gpart, sums, g.N, G, g.gT, t.bm, t.wgm);
+}
+
 // Tile shape: fewest tiles per CU times tile area times the shape's cost per
 // output element.  The costs were fitted to MI355X timings of the SDXL conv,
 // projection and fused Q/K/V shapes; L2 request traffic per MFMA falls as the
 // tile grows, which is what the larger shapes buy.
-template <bool CONV>
-void launch_bf16_auto(const GemmArgs& g, hipStream_t st) {
+int pick_tile(const GemmArgs& g) {
   const int cus = gemm_cus();
   int best = 0;
   double best_cost = 1e300;
@@ -403,7 +506,12 @@ void launch_bf16_auto(const GemmArgs& g, hipStream_t st) {
       best = c;
     }
   }
-  switch (best) {
+  return best;
+}
+
+template <bool CONV>
+void launch_bf16_auto(const GemmArgs& g, hipStream_t st) {
+  switch (pick_tile(g)) {
     case 0: launch_bf16<0, CONV>(g, st); break;
     case 1: launch_bf16<1, CONV>(g, st); break;
     case 2: launch_bf16<2, CONV>(g, st); break;
@@ -616,4 +724,59 @@ DP_API dp_status dp_qkv_projection_into_buffers(const void* x, const void* wq, c
   m.row_off[1] = m.row_off[2] = static_cast<int>(t0);
   return run_gemm(false, x, nullptr, nullptr, nullptr, 0, 0, 0, m, nullptr, B * T_loc, 3 * C, C, dt, stream,
                   name);
+}
+
+DP_API size_t dp_conv3x3_gn_sums_workspace(int64_t B, int64_t h, int64_t W, int64_t Cout) {
+  if (B <= 0 || h <= 0 || W <= 0 || Cout <= 0) return 0;
+  // partial rows: tiles_m * WGM <= M / (BM / WGM) + WGM, and BM / WGM >= 32
+  const int64_t rows = (B * h * W + 31) / 32 + 4;
+  return static_cast<size_t>(rows) * 2 * static_cast<size_t>(Cout) * sizeof(float2);
+}
+
+DP_API dp_status dp_conv3x3_stale_halo_gn_sums(const void* x, const void* halo_top, const void* halo_bot,
+                                               const void* w, const float* bias, void* y, float* gn_sums,
+                                               int64_t G, void* ws, size_t ws_bytes, int64_t B, int64_t h,
+                                               int64_t W, int64_t Cin, int64_t Cout, dp_dtype dt,
+                                               hipStream_t stream) {
+  using dp::fail;
+  const char* name = "dp_conv3x3_stale_halo_gn_sums";
+  if (!x || !w || !y || !gn_sums) return fail(DP_ERR_INVALID_ARG, "%s: NULL pointer", name);
+  if (B <= 0 || h <= 0 || W <= 0 || Cin <= 0 || Cout <= 0 || G <= 0)
+    return fail(DP_ERR_INVALID_ARG, "%s: sizes must be positive", name);
+  if (Cout % G != 0) return fail(DP_ERR_INVALID_ARG, "%s: Cout %% G != 0", name);
+  if (!dp::dtype_ok(dt)) return fail(DP_ERR_INVALID_ARG, "%s: bad dtype", name);
+  const size_t need = dp_conv3x3_gn_sums_workspace(B, h, W, Cout);
+  if (!ws || ws_bytes < need) return fail(DP_ERR_INVALID_ARG, "%s: workspace %zu < %zu bytes", name, ws_bytes, need);
+  const size_t es = dp::dtype_size(dt);
+  const size_t yb = static_cast<size_t>(B * h * W * Cout) * es, hbb = static_cast<size_t>(B * W * Cin) * es;
+  const size_t sb = static_cast<size_t>(B * G) * 8;
+  if (dp::overlaps(x, B * h * W * Cin * es, y, yb) || dp::overlaps(w, Cout * 9 * Cin * es, y, yb) ||
+      (halo_top && dp::overlaps(halo_top, hbb, y, yb)) || (halo_bot && dp::overlaps(halo_bot, hbb, y, yb)) ||
+      dp::overlaps(gn_sums, sb, y, yb) || dp::overlaps(gn_sums, sb, ws, need) || dp::overlaps(ws, need, y, yb))
+    return fail(DP_ERR_INVALID_ARG, "%s: an output overlaps an input or the workspace", name);
+  if (dt != DP_BF16 || Cin % kBK != 0 || Cin > 2048 || Cout % 32 != 0)
+    return fail(DP_ERR_UNSUPPORTED, "%s: needs bf16 with Cin %% 32 == 0, Cin <= 2048, Cout %% 32 == 0", name);
+  if (h * W < 160) return fail(DP_ERR_UNSUPPORTED, "%s: needs at least 160 tokens per batch item", name);
+  if (B * h * W > 0x7FFFFFFF || 9 * Cin > 0x7FFFFFFF) return fail(DP_ERR_UNSUPPORTED, "%s: dimension exceeds 2^31", name);
+  dp::clear_error();
+  GemmArgs g{};
+  g.geo = ConvGeom{static_cast<const bf16_t*>(x), static_cast<const bf16_t*>(halo_top),
+                   static_cast<const bf16_t*>(halo_bot), (int)h, (int)W, (int)Cin};
+  g.map = plain_map(w, y, B * h * W, Cout);
+  g.bias = bias;
+  g.M = (int)(B * h * W);
+  g.N = (int)Cout;
+  g.K = (int)(9 * Cin);
+  g.gpart = static_cast<float2*>(ws);
+  g.gT = (int)(h * W);
+  const int Gi = (int)G;
+  switch (pick_tile(g)) {
+    case 0: launch_bf16_gns<0>(g, gn_sums, Gi, stream); break;
+    case 1: launch_bf16_gns<1>(g, gn_sums, Gi, stream); break;
+    case 2: launch_bf16_gns<2>(g, gn_sums, Gi, stream); break;
+    case 3: launch_bf16_gns<3>(g, gn_sums, Gi, stream); break;
+    case 4: launch_bf16_gns<4>(g, gn_sums, Gi, stream); break;
+    default: launch_bf16_gns<5>(g, gn_sums, Gi, stream); break;
+  }
+  return dp::check_launch(name);
 }

@@ -44,6 +44,7 @@ struct GnArgs {
   const float* gamma;
   const float* beta;
   float* fresh;        // [B][G][2] or NULL
+  const float* given;  // [B][G][2] local sums computed elsewhere, or NULL (fold the partials)
   int T, C, G, tiles, tile_tokens, n_patches, rank, B, silu;
   float inv_count, eps;
 };
@@ -173,19 +174,35 @@ __device__ void block_group_sums(const float* s1, const float* s2, bool active, 
 }
 
 // Folds the tile partials of batch item b into lane sums red[q*G + g] (lane q
-// takes tiles q, q + lanes, ...); returns the lane count.  One fixed order, so
-// every block (and dp_groupnorm_sums) derives bit-identical sums.
+// takes tiles q, q + lanes, ..., in U interleaved accumulators so that U loads
+// are in flight); returns the lane count.  One fixed order, so every block
+// (and dp_groupnorm_sums) derives bit-identical sums.
 __device__ int fold_partials(const GnArgs& a, int b, float2* red) {
   const int G = a.G;
   const int lanes = G >= kThreads ? 1 : kThreads / G;
   const float2* pb = a.partial + static_cast<int64_t>(b) * a.tiles * G;
+  constexpr int U = 8;  // independent loads in flight per thread
   for (int f = threadIdx.x; f < lanes * G; f += kThreads) {
     const int g = f % G, q = f / G;
-    float2 s = make_float2(0.f, 0.f);
-    for (int t = q; t < a.tiles; t += lanes) {
-      const float2 p = pb[static_cast<int64_t>(t) * G + g];
-      s.x += p.x;
-      s.y += p.y;
+    float2 acc[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) acc[u] = make_float2(0.f, 0.f);
+    for (int t0 = q; t0 < a.tiles; t0 += U * lanes) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int t = t0 + u * lanes;
+        if (t < a.tiles) {
+          const float2 p = pb[static_cast<int64_t>(t) * G + g];
+          acc[u].x += p.x;
+          acc[u].y += p.y;
+        }
+      }
+    }
+    float2 s = acc[0];
+#pragma unroll
+    for (int u = 1; u < U; ++u) {
+      s.x += acc[u].x;
+      s.y += acc[u].y;
     }
     red[f] = s;
   }
@@ -303,7 +320,13 @@ __global__ void __launch_bounds__(kThreads) gn_apply(GnArgs a) {
   for (int u = 0; u < kUnroll; ++u)
     first[u] = load_or_zero<BF16>(a, b, t_begin + tl + u * tpp, t_end, vi, active && u < npass);
 
-  const int lanes = fold_partials(a, b, red);
+  int lanes = 1;
+  if (a.given) {  // the local sums come from the caller: one lane holding them
+    for (int g = tid; g < G; g += kThreads)
+      red[g] = make_float2(a.given[(static_cast<int64_t>(b) * G + g) * 2], a.given[(static_cast<int64_t>(b) * G + g) * 2 + 1]);
+  } else {
+    lanes = fold_partials(a, b, red);
+  }
   __syncthreads();
   finalize_stats(a, b, tile, lanes, red, gstat);
   __syncthreads();
@@ -408,7 +431,7 @@ DP_API dp_status dp_groupnorm_stale_stats(const void* x, const float* stale_sums
   if (dp::overlaps(x, xb, y, xb)) return fail(DP_ERR_INVALID_ARG, "dp_groupnorm_stale_stats: x and y overlap");
 
   const GnPlan p = make_plan(B, T_loc, C, dt);
-  GnArgs ga;
+  GnArgs ga{};
   ga.x = x;
   ga.y = y;
   ga.partial = static_cast<float2*>(ws);
@@ -472,5 +495,50 @@ DP_API dp_status dp_groupnorm_sums(const void* x, float* sums_out, int64_t B, in
   if (dt == DP_BF16) hipLaunchKernelGGL(gn_partial<true>, grid, dim3(kThreads), 0, stream, ga);
   else hipLaunchKernelGGL(gn_partial<false>, grid, dim3(kThreads), 0, stream, ga);
   hipLaunchKernelGGL(gn_sums, dim3(1, static_cast<unsigned>(B)), dim3(kThreads), 0, stream, ga);
+  return dp::check_launch(name);
+}
+
+DP_API dp_status dp_groupnorm_apply(const void* x, const float* local_sums, const float* stale_sums,
+                                    int64_t n_patches, int64_t rank, int64_t T_total, const float* gamma,
+                                    const float* beta, float eps, int fuse_silu, void* y, int64_t B, int64_t T_loc,
+                                    int64_t C, int64_t G, dp_dtype dt, hipStream_t stream) {
+  using dp::fail;
+  const char* name = "dp_groupnorm_apply";
+  if (!x || !y || !local_sums) return fail(DP_ERR_INVALID_ARG, "%s: NULL x, y or local_sums", name);
+  if (B <= 0 || T_loc <= 0 || C <= 0 || G <= 0 || n_patches <= 0) return fail(DP_ERR_INVALID_ARG, "%s: sizes must be positive", name);
+  if (!stale_sums && n_patches > 1) return fail(DP_ERR_INVALID_ARG, "%s: NULL stale_sums with %lld patches", name, (long long)n_patches);
+  if (rank < 0 || rank >= n_patches) return fail(DP_ERR_INVALID_ARG, "%s: rank outside [0, n_patches)", name);
+  if (T_total < T_loc) return fail(DP_ERR_INVALID_ARG, "%s: T_total < T_loc", name);
+  if (!(eps >= 0.f)) return fail(DP_ERR_INVALID_ARG, "%s: eps must be >= 0", name);
+  if (C % G != 0) return fail(DP_ERR_INVALID_ARG, "%s: C %% G != 0", name);
+  if (!dp::dtype_ok(dt)) return fail(DP_ERR_INVALID_ARG, "%s: bad dtype", name);
+  const int vec = dt == DP_BF16 ? 8 : 4;
+  if (C % vec != 0 || C > 2048 || C / vec > kThreads || T_loc > 0x7FFFFFFF || B > 65535 || B * G > 0x7FFFFFFF)
+    return fail(DP_ERR_UNSUPPORTED, "%s: C=%lld G=%lld not supported", name, (long long)C, (long long)G);
+  const size_t xb = static_cast<size_t>(B * T_loc * C) * dp::dtype_size(dt);
+  if (dp::overlaps(x, xb, y, xb)) return fail(DP_ERR_INVALID_ARG, "%s: x and y overlap", name);
+  const GnPlan p = make_plan(B, T_loc, C, dt);
+  GnArgs ga{};
+  ga.x = x;
+  ga.y = y;
+  ga.given = local_sums;
+  ga.stale = stale_sums;
+  ga.gamma = gamma;
+  ga.beta = beta;
+  ga.T = static_cast<int>(T_loc);
+  ga.C = static_cast<int>(C);
+  ga.G = static_cast<int>(G);
+  ga.tiles = p.tiles;
+  ga.tile_tokens = p.tile_tokens;
+  ga.n_patches = static_cast<int>(n_patches);
+  ga.rank = static_cast<int>(rank);
+  ga.B = static_cast<int>(B);
+  ga.silu = fuse_silu;
+  ga.inv_count = static_cast<float>(1.0 / (static_cast<double>(T_total) * (C / G)));
+  ga.eps = eps;
+  dp::clear_error();
+  const dim3 grid(static_cast<unsigned>(p.tiles), static_cast<unsigned>(B));
+  if (dt == DP_BF16) hipLaunchKernelGGL(gn_apply<true>, grid, dim3(kThreads), 0, stream, ga);
+  else hipLaunchKernelGGL(gn_apply<false>, grid, dim3(kThreads), 0, stream, ga);
   return dp::check_launch(name);
 }

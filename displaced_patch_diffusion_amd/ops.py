@@ -139,6 +139,48 @@ def dp_groupnorm_sums(x, G: int = 32, out=None, ws=None):
     return out
 
 
+def dp_groupnorm_apply(x, local_sums, stale_sums, rank: int, T_total: int, gamma=None, beta=None,
+                       eps: float = 1e-5, silu: bool = False, G: int = 32, y=None):
+    """GroupNorm of x [B,T_loc,C] from the caller's local sums [B,G,2] plus the
+    other patches' stale sums [N,B,G,2]."""
+    _dev(x, y, f32=(local_sums, stale_sums, gamma, beta))
+    dt = _dt(x, y)
+    B, T_loc, C = x.shape
+    n_patches = 1 if stale_sums is None else stale_sums.shape[0]
+    if y is None:
+        y = torch.empty_like(x)
+    check(lib().dp_groupnorm_apply(_p(x), _p(local_sums), _p(stale_sums), n_patches, rank, T_total, _p(gamma),
+                                   _p(beta), eps, int(silu), _p(y), B, T_loc, C, G, dt, _stream()),
+          "dp_groupnorm_apply")
+    return y
+
+
+def dp_conv3x3_gn_sums_workspace(B, h, W, Cout) -> int:
+    return lib().dp_conv3x3_gn_sums_workspace(B, h, W, Cout)
+
+
+def dp_conv3x3_stale_halo_gn_sums(x, halo_top, halo_bot, w, bias=None, G: int = 32, y=None, gn_sums=None, ws=None):
+    """conv3x3 of x [B,h,W,Cin] (as dp_conv3x3_stale_halo) plus the GroupNorm
+    sums [B,G,2] of its output.  Returns (y, gn_sums)."""
+    _dev(x, halo_top, halo_bot, w, y, ws, f32=(bias, gn_sums))
+    dt = _dt(x, halo_top, halo_bot, w, y)
+    B, h, W, Cin = x.shape
+    Cout = w.shape[0]
+    if w.shape != (Cout, 3, 3, Cin):
+        raise ValueError("w must be [Cout,3,3,Cin]")
+    if y is None:
+        y = torch.empty((B, h, W, Cout), dtype=x.dtype, device=x.device)
+    if gn_sums is None:
+        gn_sums = torch.empty((B, G, 2), dtype=torch.float32, device=x.device)
+    if ws is None:
+        ws = _ws(dp_conv3x3_gn_sums_workspace(B, h, W, Cout), x.device)
+    check(lib().dp_conv3x3_stale_halo_gn_sums(_p(x), _p(halo_top), _p(halo_bot), _p(w), _p(bias), _p(y),
+                                              _p(gn_sums), G, _p(ws), 0 if ws is None else ws.numel(),
+                                              B, h, W, Cin, Cout, dt, _stream()),
+          "dp_conv3x3_stale_halo_gn_sums")
+    return y, gn_sums
+
+
 def dp_linear(x, w, bias=None, y=None):
     """x [..., Cin], w [Cout, Cin] -> y [..., Cout]."""
     _dev(x, w, y, f32=(bias,))

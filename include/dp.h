@@ -120,6 +120,31 @@ dp_status dp_conv3x3_stale_halo(const void* x, const void* halo_top, const void*
                                 dp_dtype dt, hipStream_t stream);
 
 /*
+ * The displaced 3x3 convolution of dp_conv3x3_stale_halo, which also returns
+ * the GroupNorm sums of its output, so the GroupNorm that follows needs no
+ * read pass of its own to form them (the conv output feeds the displaced
+ * GroupNorm, "OTIL ...", "What is implemented where").
+ * y is exactly what dp_conv3x3_stale_halo writes.  gn_sums[b, g, :] =
+ * (sum y, sum y^2) of the stored (bf16) outputs of batch item b over the h*W
+ * tokens and the Cout/G channels of group g, float32, accumulated per output
+ * tile in the conv epilogue and folded in a fixed order (deterministic; equal
+ * to dp_groupnorm_sums of y up to float32 rounding order).
+ * gn_sums [B, G, 2] float32; ws/ws_bytes: caller-owned device scratch of at
+ * least dp_conv3x3_gn_sums_workspace(B, h, W, Cout) bytes; other arguments as
+ * dp_conv3x3_stale_halo.
+ * Supported: bf16 with Cin % 32 == 0, Cin <= 2048, Cout % 32 == 0 and
+ * h*W >= 160.  Errors: INVALID_ARG for NULL x/w/y/gn_sums, sizes <= 0,
+ * Cout % G != 0, a short workspace or overlapping buffers; UNSUPPORTED
+ * otherwise (f32 included: use dp_conv3x3_stale_halo then dp_groupnorm_sums).
+ */
+size_t dp_conv3x3_gn_sums_workspace(int64_t B, int64_t h, int64_t W, int64_t Cout);
+dp_status dp_conv3x3_stale_halo_gn_sums(const void* x, const void* halo_top, const void* halo_bot,
+                                        const void* w, const float* bias, void* y, float* gn_sums,
+                                        int64_t G, void* ws, size_t ws_bytes, int64_t B, int64_t h,
+                                        int64_t W, int64_t Cin, int64_t Cout, dp_dtype dt,
+                                        hipStream_t stream);
+
+/*
  * GroupNorm of the rank's tokens with statistics of the whole image: fresh
  * sums over the local tokens plus the stale sums the other patches produced
  * one step earlier ("OTIL ...", "What is implemented where": two scalars per
@@ -164,6 +189,21 @@ dp_status dp_groupnorm_stale_stats(const void* x, const float* stale_sums, int64
  */
 dp_status dp_groupnorm_sums(const void* x, float* sums_out, int64_t B, int64_t T_loc, int64_t C,
                             int64_t G, dp_dtype dt, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * The normalising half of dp_groupnorm_stale_stats, with the rank's local sums
+ * supplied by the caller (from dp_conv3x3_stale_halo_gn_sums or
+ * dp_groupnorm_sums): one pass over x, no workspace.  Statistics, output and
+ * SiLU as dp_groupnorm_stale_stats with S = local_sums + sum_{p != rank}
+ * stale_sums[p]; given the sums dp_groupnorm_sums returns for x, y equals
+ * dp_groupnorm_stale_stats's bit for bit.
+ * local_sums [B, G, 2] float32; other arguments as dp_groupnorm_stale_stats.
+ * Errors: as dp_groupnorm_stale_stats, plus INVALID_ARG for NULL local_sums.
+ */
+dp_status dp_groupnorm_apply(const void* x, const float* local_sums, const float* stale_sums,
+                             int64_t n_patches, int64_t rank, int64_t T_total, const float* gamma,
+                             const float* beta, float eps, int fuse_silu, void* y, int64_t B,
+                             int64_t T_loc, int64_t C, int64_t G, dp_dtype dt, hipStream_t stream);
 
 /*
  * Dense projection of the rank's own rows (the Q/K/V and output projections

@@ -177,3 +177,34 @@ def test_otil_validation(lib):
     # the other calls reject F16
     assert status_and_error(lib.dp_linear, A, Bp, None, Cp, 4, 32, 32, _lib.DP_F16, None)[0] == \
         _lib.DP_ERR_INVALID_ARG
+
+
+def test_conv_gn_sums_and_apply_validation(lib):
+    F2, G2 = 0x60000000, 0x70000000
+    f = lib.dp_conv3x3_stale_halo_gn_sums
+    need = lib.dp_conv3x3_gn_sums_workspace(2, 30, 240, 640)
+    assert need >= (2 * 30 * 240 // 32) * 2 * 640 * 8
+    ok = [A, None, None, Bp, None, Cp, D, 32, E, need, 2, 30, 240, 640, 640, _lib.DP_BF16, None]
+
+    def call(i=None, v=None):
+        a = list(ok)
+        if i is not None:
+            a[i] = v
+        return status_and_error(f, *a)
+
+    assert call(6, None)[0] == _lib.DP_ERR_INVALID_ARG              # NULL gn_sums
+    assert call(7, 48)[0] == _lib.DP_ERR_INVALID_ARG                # Cout % G != 0
+    assert call(9, need - 1)[0] == _lib.DP_ERR_INVALID_ARG          # short workspace
+    assert call(15, _lib.DP_F32)[0] == _lib.DP_ERR_UNSUPPORTED       # bf16 only
+    a = list(ok)
+    a[11], a[12] = 1, 100                                           # h*W = 100 < 160
+    a[9] = lib.dp_conv3x3_gn_sums_workspace(2, 1, 100, 640)
+    assert status_and_error(f, *a)[0] == _lib.DP_ERR_UNSUPPORTED
+    assert call(6, Cp + 64)[0] == _lib.DP_ERR_INVALID_ARG           # gn_sums inside y
+    ap = lib.dp_groupnorm_apply
+    st, _ = status_and_error(ap, A, None, F2, 4, 1, 1000, None, None, 1e-5, 0, G2, 2, 100, 64, 32,
+                             _lib.DP_BF16, None)
+    assert st == _lib.DP_ERR_INVALID_ARG                             # NULL local sums
+    st, _ = status_and_error(ap, A, Bp, F2, 4, 4, 1000, None, None, 1e-5, 0, G2, 2, 100, 64, 32,
+                             _lib.DP_BF16, None)
+    assert st == _lib.DP_ERR_INVALID_ARG                             # rank outside [0, 4)
