@@ -752,7 +752,9 @@ DP_API dp_status dp_conv3x3_stale_halo_gn_sums(const void* x, const void* halo_t
   const size_t sb = static_cast<size_t>(B * G) * 8;
   if (dp::overlaps(x, B * h * W * Cin * es, y, yb) || dp::overlaps(w, Cout * 9 * Cin * es, y, yb) ||
       (halo_top && dp::overlaps(halo_top, hbb, y, yb)) || (halo_bot && dp::overlaps(halo_bot, hbb, y, yb)) ||
-      dp::overlaps(gn_sums, sb, y, yb) || dp::overlaps(gn_sums, sb, ws, need) || dp::overlaps(ws, need, y, yb))
+      dp::overlaps(gn_sums, sb, y, yb) || dp::overlaps(gn_sums, sb, ws, need) || dp::overlaps(ws, need, y, yb) ||
+      dp::overlaps(gn_sums, sb, x, B * h * W * Cin * es) || dp::overlaps(gn_sums, sb, w, Cout * 9 * Cin * es) ||
+      dp::overlaps(ws, need, x, B * h * W * Cin * es) || dp::overlaps(ws, need, w, Cout * 9 * Cin * es))
     return fail(DP_ERR_INVALID_ARG, "%s: an output overlaps an input or the workspace", name);
   if (dt != DP_BF16 || Cin % kBK != 0 || Cin > 2048 || Cout % 32 != 0)
     return fail(DP_ERR_UNSUPPORTED, "%s: needs bf16 with Cin %% 32 == 0, Cin <= 2048, Cout %% 32 == 0", name);

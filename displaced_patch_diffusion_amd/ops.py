@@ -166,8 +166,11 @@ def dp_conv3x3_stale_halo_gn_sums(x, halo_top, halo_bot, w, bias=None, G: int = 
     dt = _dt(x, halo_top, halo_bot, w, y)
     B, h, W, Cin = x.shape
     Cout = w.shape[0]
-    if w.shape != (Cout, 3, 3, Cin):
+    if tuple(w.shape) != (Cout, 3, 3, Cin):
         raise ValueError("w must be [Cout,3,3,Cin]")
+    for hl in (halo_top, halo_bot):
+        if hl is not None and tuple(hl.shape) != (B, W, Cin):
+            raise ValueError("halo must be [B,W,Cin]")
     if y is None:
         y = torch.empty((B, h, W, Cout), dtype=x.dtype, device=x.device)
     if gn_sums is None:
