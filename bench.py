@@ -549,6 +549,9 @@ def main():
                 "unit": "TFLOP/s", "frac": round(achieved / peak_mfma, 4),
                 "traffic": _traffic_from_profile(w), "kernel": "attn_bf16_d64",
                 "work_per_launch": f"{fl['attn'] / 1e9:.2f} GFLOP"}
+    props = torch.cuda.get_device_properties(0)
+    device = {"name": props.name, "arch": getattr(props, "gcnArchName", ""), "compute_units": props.multi_processor_count,
+              "hbm_GiB": round(props.total_memory / 2 ** 30, 1)}
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": K, "warmup": args.warmup, "ms_per_step": round(step_s * 1e3, 4),
@@ -559,6 +562,7 @@ def main():
                    "conv_level": f"{w.conv_H}x{w.conv_W}", "C_conv": w.conv_C, "n_patches": w.N,
                    "rank": w.rank, "Tq": w.Tq, "T_kv": w.T_kv, "qkv": args.qkv, "gn_sums": args.gn_sums,
                    "parallelism": "one rank's share, 1 GPU"},
+        "device": device,
         "roofline": roofline,
         "kernels": kern,
         "groupnorm_GBps": kern.get("groupnorm", {}).get("GB/s"),
