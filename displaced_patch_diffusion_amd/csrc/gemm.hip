@@ -10,10 +10,10 @@
 // Reduction index of the conv: k = tap * Cin + c with tap = (dy+1)*3 + (dx+1),
 // matching the [Cout, 3, 3, Cin] weight layout, so weight rows are K-contiguous.
 //
-// bf16 path (gfx950): a 256-thread block computes one output tile of a shape
-// chosen per problem so the tiles spread evenly over the CUs (128x128, 64x128,
-// 64x64, 160x128, 96x128 or 128x160); tiles sharing A rows are dealt to one
-// XCD.  K moves through an LDS ring by direct global->LDS loads issued ahead, 64
+// bf16 path (gfx950): a block of NW waves (4 in every shape used) computes one
+// output tile of a shape chosen per problem so the tiles spread evenly over the
+// CUs (128x128, 64x128, 64x64, 160x128, 96x128 or 128x160); tiles sharing A
+// rows are dealt to one XCD.  K moves through an LDS ring by direct global->LDS loads issued ahead, 64
 // of K per stage (128-byte rows, one L2 line each) or 32 when K or Cin is not a
 // multiple of 64.  LDS rows are XOR-swizzled.  Each wave owns a quarter of the tile as
 // v_mfma_f32_32x32x16_bf16 blocks computed as (W rows) x (A rows)^T, so an
@@ -106,31 +106,31 @@ struct Stage {
   static constexpr int value = S;
 };
 
-// One block computes a BM x BN output tile with 4 waves arranged WGM x WGN
-// (WGM * WGN = 4); each wave owns (BM/WGM) x (BN/WGN) as 32 x 32 MFMA blocks
+// One block computes a BM x BN output tile with NW waves arranged WGM x WGN
+// (WGM * WGN = NW); each wave owns (BM/WGM) x (BN/WGN) as 32 x 32 MFMA blocks
 // computed as (W rows) x (A rows)^T, so an accumulator lane holds 4
 // consecutive output channels of one output row.  K advances BK (32 or 64) per
 // stage through an ST-stage LDS ring.
 //
 // DMA: a stage is BM A rows followed by BN W rows of BK bf16 (RB = 2*BK bytes,
 // one L2 line when BK = 64), cut into 1 KB slabs; slab s is loaded by wave
-// s % 4 with one instruction in which RB/16 consecutive lanes fetch one row.
-// When the slab count is not a multiple of 4 the first waves own one slab
+// s % NW with one instruction in which RB/16 consecutive lanes fetch one row.
+// When the slab count is not a multiple of NW the first waves own one slab
 // more, and each wave waits on its own outstanding count.
-template <int BM, int BN, int WGM, int BK, int ST, int OCC, bool CONV, bool GNS = false>
-__global__ void __launch_bounds__(kThreads, OCC) gemm_bf16(GemmArgs g) {
-  constexpr int WGN = 4 / WGM;
+template <int BM, int BN, int WGM, int NW, int BK, int ST, int OCC, bool CONV, bool GNS = false>
+__global__ void __launch_bounds__(64 * NW, OCC) gemm_bf16(GemmArgs g) {
+  constexpr int WGN = NW / WGM;
   constexpr int RB = BK * 2, LPR = RB / 16, RPS = 64 / LPR;  // row bytes, lanes per row, rows per slab
   constexpr int kABytes = BM * RB;
   constexpr int kStageBytes = (BM + BN) * RB;
   constexpr int kASl = BM / RPS, kSl = (BM + BN) / RPS;    // slabs: A first, then W
-  constexpr int kJ = (kSl + 3) / 4;                        // slab slots per wave
-  constexpr int kRem = kSl % 4;                            // waves < kRem own kJ slabs, the rest kJ - 1
+  constexpr int kJ = (kSl + NW - 1) / NW;                  // slab slots per wave
+  constexpr int kRem = kSl % NW;                           // waves < kRem own kJ slabs, the rest kJ - 1
   constexpr int kDmaHi = kJ, kDmaLo = kRem ? kJ - 1 : kJ;  // DMAs per stage per wave
   constexpr int kQ = BK / 16;                              // 16-wide MFMA k steps per stage
   constexpr int WM = BM / WGM, WN = BN / WGN, MB = WM / 32, NB = WN / 32;
   static_assert(BK == 32 || BK == 64, "slice width");
-  static_assert(WGM * WGN == 4 && WM % 32 == 0 && WN % 32 == 0 && BM % RPS == 0 && BN % RPS == 0, "tile");
+  static_assert(WGM * WGN == NW && WM % 32 == 0 && WN % 32 == 0 && BM % RPS == 0 && BN % RPS == 0, "tile");
   __shared__ __attribute__((aligned(1024))) char lds[ST * kStageBytes];
 
   const int u = (blockIdx.x % kXcds) * g.units_per_xcd + blockIdx.x / kXcds;
@@ -151,7 +151,7 @@ __global__ void __launch_bounds__(kThreads, OCC) gemm_bf16(GemmArgs g) {
   bool has[kJ], is_a[kJ], a_ok[kJ];
 #pragma unroll
   for (int j = 0; j < kJ; ++j) {
-    const int sl = 4 * j + wave;
+    const int sl = NW * j + wave;
     has[j] = sl < kSl;
     is_a[j] = sl < kASl;
     const int row = RPS * (is_a[j] ? sl : sl - kASl) + lane / LPR;
@@ -216,7 +216,7 @@ __global__ void __launch_bounds__(kThreads, OCC) gemm_bf16(GemmArgs g) {
 #pragma unroll
     for (int j = 0; j < kJ; ++j) {
       if (!has[j]) continue;
-      gdma16(src[j], lds0 + st * kStageBytes + j * 4096);
+      gdma16(src[j], lds0 + st * kStageBytes + j * (NW * 1024));
       src[j] += RB;
     }
     if constexpr (CONV) {
@@ -445,12 +445,12 @@ int gemm_cus() {
 // K % 64 == 0 (else 32-wide slices in a 3-stage ring), blocks per CU for the
 // launch bounds, relative time per output element (fitted to MI355X timings).
 struct TileCfg {
-  int bm, bn, wgm, bk, st, occ;
+  int bm, bn, wgm, nw, bk, st, occ;
   double cost_per_elem;
 };
 constexpr TileCfg kTiles[] = {
-    {128, 128, 2, 64, 2, 2, 1.0},   {64, 128, 2, 64, 3, 2, 1.19},  {64, 64, 2, 64, 3, 2, 1.23},
-    {160, 128, 1, 64, 2, 2, 0.875}, {96, 128, 1, 32, 3, 3, 1.07},  {128, 160, 4, 64, 2, 2, 0.94},
+    {128, 128, 2, 4, 64, 2, 2, 1.0},   {64, 128, 2, 4, 64, 3, 2, 1.19},  {64, 64, 2, 4, 64, 3, 2, 1.23},
+    {160, 128, 1, 4, 64, 2, 2, 0.875}, {96, 128, 1, 4, 32, 3, 3, 1.07},  {128, 160, 4, 4, 64, 2, 2, 0.94},
 };
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 
@@ -464,9 +464,9 @@ void launch_bf16(const GemmArgs& base, hipStream_t st) {
   g.units_per_xcd = (g.units + kXcds - 1) / kXcds;
   const dim3 grid(static_cast<unsigned>(g.units_per_xcd * kXcds));
   if (g.K % t.bk == 0)
-    hipLaunchKernelGGL((gemm_bf16<t.bm, t.bn, t.wgm, t.bk, t.st, t.occ, CONV>), grid, dim3(kThreads), 0, st, g);
+    hipLaunchKernelGGL((gemm_bf16<t.bm, t.bn, t.wgm, t.nw, t.bk, t.st, t.occ, CONV>), grid, dim3(64 * t.nw), 0, st, g);
   else
-    hipLaunchKernelGGL((gemm_bf16<t.bm, t.bn, t.wgm, kBK, kStages, t.occ, CONV>), grid, dim3(kThreads), 0, st, g);
+    hipLaunchKernelGGL((gemm_bf16<t.bm, t.bn, t.wgm, t.nw, kBK, kStages, t.occ, CONV>), grid, dim3(64 * t.nw), 0, st, g);
 }
 
 // Conv with GroupNorm partials: same tile choice, GNS epilogue, then the fold.
@@ -480,9 +480,9 @@ void launch_bf16_gns(const GemmArgs& base, float* sums, int G, hipStream_t st) {
   g.units_per_xcd = (g.units + kXcds - 1) / kXcds;
   const dim3 grid(static_cast<unsigned>(g.units_per_xcd * kXcds));
   if (g.K % t.bk == 0)
-    hipLaunchKernelGGL((gemm_bf16<t.bm, t.bn, t.wgm, t.bk, t.st, t.occ, true, true>), grid, dim3(kThreads), 0, st, g);
+    hipLaunchKernelGGL((gemm_bf16<t.bm, t.bn, t.wgm, t.nw, t.bk, t.st, t.occ, true, true>), grid, dim3(64 * t.nw), 0, st, g);
   else
-    hipLaunchKernelGGL((gemm_bf16<t.bm, t.bn, t.wgm, kBK, kStages, t.occ, true, true>), grid, dim3(kThreads), 0, st, g);
+    hipLaunchKernelGGL((gemm_bf16<t.bm, t.bn, t.wgm, t.nw, kBK, kStages, t.occ, true, true>), grid, dim3(64 * t.nw), 0, st, g);
   const int B = g.M / g.gT;
   hipLaunchKernelGGL(gn_conv_fold, dim3(static_cast<unsigned>(G), static_cast<unsigned>(B)), dim3(kFoldThreads), 0, st,
                      g.gpart, sums, g.N, G, g.gT, t.bm, t.wgm);
