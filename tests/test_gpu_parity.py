@@ -60,6 +60,9 @@ def test_splice_bit_exact(dt, B, T_kv, C, t0, T_loc):
     ("bf16", 16406, 96, 96, False),   # 96x128, 32-wide slices
     ("bf16", 20513, 128, 160, True),  # 128x160
     ("bf16", 20513, 96, 160, False),  # 128x160 with 32-wide slices (K % 64 != 0)
+    ("bf16", 9810, 64, 640, True),    # 128x128, five column tiles
+    ("bf16", 5000, 96, 640, False),   # 128x128 with 32-wide slices
+    ("bf16", 18468, 128, 512, True),  # 160x128, four column tiles
     ("f32", 300, 64, 64, True), ("f32", 77, 50, 30, False),
 ])
 def test_linear(dt, M, Cin, Cout, bias):
@@ -78,6 +81,8 @@ def test_linear(dt, M, Cin, Cout, bias):
     ("bf16", 2, 3, 50, 96, 320, "both"), ("bf16", 1, 2, 200, 32, 64, "top"),
     ("bf16", 1, 41, 400, 64, 160, "both"),   # 160x128 tiles, ragged M
     ("bf16", 2, 13, 789, 64, 160, "bottom"), # 128x160 tiles, ragged M
+    ("bf16", 1, 41, 451, 64, 512, "both"),   # 160x128 tiles, four column tiles
+    ("bf16", 1, 20, 491, 32, 640, "top"),    # 128x128 tiles, 32-wide K slices
     ("f32", 2, 16, 32, 64, 64, "both"), ("f32", 1, 2, 5, 6, 7, "top"),
 ])
 def test_conv3x3(dt, B, h, W, Cin, Cout, halos):
