@@ -208,3 +208,40 @@ def test_conv_gn_sums_and_apply_validation(lib):
     st, _ = status_and_error(ap, A, Bp, F2, 4, 4, 1000, None, None, 1e-5, 0, G2, 2, 100, 64, 32,
                              _lib.DP_BF16, None)
     assert st == _lib.DP_ERR_INVALID_ARG                             # rank outside [0, 4)
+
+
+# Fake addresses 16 TB apart, so that the overlap checks pass for the huge
+# sizes below and the size limits are what rejects each call.
+FAR = [(i + 1) << 44 for i in range(8)]
+
+
+def test_size_limits_are_rejected_before_launch(lib):
+    """Every entry point refuses shapes beyond the 32-bit ranges its kernels
+    index with (grid dimensions, buffer-descriptor byte counts, int rows)."""
+    a, b, c, d, e, f, g, h = FAR
+    bf = _lib.DP_BF16
+    # attention: one batch item of K/V beyond 2^31 elements; more than 65535 heads
+    st, msg = status_and_error(lib.dp_attn_stale_kv, a, b, c, d, 1, 10, 64, 4_000_000, 64, 0.0, bf,
+                               None, 0, None)
+    assert st == _lib.DP_ERR_UNSUPPORTED and "2^31" in msg
+    st, _ = status_and_error(lib.dp_attn_stale_kv, a, b, c, d, 1, 70_000, 64, 64, 64, 0.0, bf, None, 0, None)
+    assert st == _lib.DP_ERR_UNSUPPORTED
+    # projection with 2^31 rows
+    st, msg = status_and_error(lib.dp_linear, a, b, None, c, 1 << 31, 64, 64, bf, None)
+    assert st == _lib.DP_ERR_UNSUPPORTED and "2^31" in msg
+    # conv whose B*h*W reaches 2^32 rows
+    st, msg = status_and_error(lib.dp_conv3x3_stale_halo, a, None, None, b, None, c, 2, 1 << 30, 2, 64, 64,
+                               bf, None)
+    assert st == _lib.DP_ERR_UNSUPPORTED and "2^31" in msg
+    # fused Q/K/V projection into buffers of B*T_kv beyond 2^31 rows
+    st, msg = status_and_error(lib.dp_qkv_projection_into_buffers, a, b, c, d, e, f, g, 2, 64, 1 << 30, 0, 64,
+                               bf, None)
+    assert st == _lib.DP_ERR_UNSUPPORTED and "2^31" in msg
+    # GroupNorm over 2^31 local tokens (given a large enough workspace)
+    need = lib.dp_groupnorm_stale_stats_workspace(1, 1 << 31, 64, 32)
+    st, _ = status_and_error(lib.dp_groupnorm_stale_stats, a, None, 1, 0, 1 << 31, None, None, 1e-5, 0, b, None,
+                             1, 1 << 31, 64, 32, bf, c, need, None)
+    assert st == _lib.DP_ERR_UNSUPPORTED
+    # splice with more (batch, K/V) segments than a grid dimension holds
+    st, msg = status_and_error(lib.dp_kv_buffer_splice, a, b, c, d, 40_000, 16, 8, 0, 4, bf, None)
+    assert st == _lib.DP_ERR_UNSUPPORTED and "grid" in msg
