@@ -30,6 +30,14 @@
 // product; row sums and O accumulate in float32; output rows are normalised
 // once at the end.
 //
+// Schedules.  A unit is (batch, head, 128-query block) against all keys.  The
+// split schedule gives each block one unit, or one of S equal key chunks of
+// it (partials merged by attn_combine), with the blocks of one key chunk
+// resident together on one XCD.  When the units do not fill whole rounds of
+// resident blocks, the balanced schedule gives each resident block an equal
+// contiguous range of the (unit, key tile) sequence; attn_combine_sk merges
+// the pieces of the units that neighbouring blocks share.
+//
 // f32 (d = 32 or 64)
 // ------------------
 // One thread per query, K/V tiles of 32 keys in LDS, the same online softmax
@@ -38,6 +46,8 @@
 
 #include <algorithm>
 #include <cmath>
+#include <cstdlib>
+#include <cstring>
 
 #include "dp_internal.h"
 
@@ -71,7 +81,20 @@ struct AttnArgs {
   int B, H, Tq, Tkv;
   float c;          // scale * log2(e)
   int n_qblk, n_split, chunk_tiles, n_tiles, units, units_per_xcd;
+  int sk;           // 1: balanced contiguous work ranges per block (see attn_bf16_d64)
+  int sk_grid;      // blocks of the balanced schedule (a multiple of kXcds)
+  long long work;   // units * n_tiles (balanced schedule)
 };
+
+// Balanced schedule: block position p owns the work items
+// [sk_start(p), sk_start(p+1)) of the (unit, tile) sequence.
+__device__ __host__ __forceinline__ long long sk_start(long long p, long long work, long long grid) {
+  return p * work / grid;
+}
+// Position owning work item w: the largest p with sk_start(p) <= w.
+__device__ __host__ __forceinline__ long long sk_owner(long long w, long long work, long long grid) {
+  return ((w + 1) * grid - 1) / work;
+}
 
 __device__ __forceinline__ bf16x8 pack8(const f32x16& s, int base) {
   u32x4 u;
@@ -116,26 +139,16 @@ struct Stage {
   static constexpr int value = S;
 };
 
-__global__ void __launch_bounds__(256, 3) attn_bf16_d64(AttnArgs a) {
-  // K tiles at stage*8 KB, V tiles at 24 KB + stage*8 KB.
-  __shared__ __attribute__((aligned(1024))) char lds[kStages * 2 * kTileBytes];
+// One segment: the queries of block qb of (b, h) against key tiles
+// [t_begin, t_end).  Split schedule (SK false): `piece` is the key chunk;
+// with one chunk the normalised bf16 rows go to out, otherwise unnormalised
+// float32 rows and (m_ref, row sum) go to the chunk's partial arrays.
+// Balanced schedule (SK true): `piece` < 0 writes out; otherwise it is the
+// partial slot of the rows.
+template <bool SK>
+__device__ __forceinline__ void attn_segment(const AttnArgs& a, char* lds, int b, int h, int qb, int t_begin,
+                                             int t_end, long long piece) {
   constexpr int kVring = kStages * kTileBytes;
-
-  // Work unit: blocks are dealt to the XCDs round-robin, so XCD x receives
-  // blocks x, x+8, ...; give each XCD a contiguous run of units.  Units are
-  // ordered (batch, head, key chunk, query block), so the blocks resident on
-  // one XCD share a key chunk and read it from that XCD's L2.
-  const int u = (blockIdx.x % kXcds) * a.units_per_xcd + blockIdx.x / kXcds;
-  if (u >= a.units) return;
-  const int qb = u % a.n_qblk;
-  int rest = u / a.n_qblk;
-  const int split = rest % a.n_split;
-  rest /= a.n_split;
-  const int h = rest % a.H;
-  const int b = rest / a.H;
-  const int t_begin = split * a.chunk_tiles;
-  const int t_end = min(a.n_tiles, t_begin + a.chunk_tiles);
-
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, g = lane >> 5;
   const int C = a.H * kD;
@@ -387,7 +400,7 @@ __global__ void __launch_bounds__(256, 3) attn_bf16_d64(AttnArgs a) {
 
   const float l_tot = swap_sum(l_part);
   if (!q_ok) return;
-  if (a.n_split == 1) {
+  if (SK ? piece < 0 : a.n_split == 1) {
     const float inv = 1.0f / l_tot;
     bf16_t* op = a.out + (static_cast<int64_t>(b) * a.Tq + qi) * C + h * kD;
 #pragma unroll
@@ -400,7 +413,16 @@ __global__ void __launch_bounds__(256, 3) attn_bf16_d64(AttnArgs a) {
         *reinterpret_cast<u32x2*>(op + d) = pk;
       }
   } else {
-    float* op = a.part_o + ((static_cast<int64_t>(split) * a.B + b) * a.Tq + qi) * C + h * kD;
+    float* op;
+    float* ml;
+    if constexpr (SK) {
+      const int64_t row = piece * kBMq + (qi - qb * kBMq);
+      op = a.part_o + row * kD;
+      ml = a.part_ml + row * 2;
+    } else {
+      op = a.part_o + ((piece * a.B + b) * a.Tq + qi) * C + h * kD;
+      ml = a.part_ml + (((piece * a.B + b) * a.H + h) * a.Tq + qi) * 2;
+    }
 #pragma unroll
     for (int db = 0; db < 2; ++db)
 #pragma unroll
@@ -410,9 +432,58 @@ __global__ void __launch_bounds__(256, 3) attn_bf16_d64(AttnArgs a) {
             f32x4{o[db][4 * qq], o[db][4 * qq + 1], o[db][4 * qq + 2], o[db][4 * qq + 3]};
       }
     if (g == 0) {
-      float* ml = a.part_ml + (((static_cast<int64_t>(split) * a.B + b) * a.H + h) * a.Tq + qi) * 2;
       ml[0] = m_ref;
       ml[1] = l_tot;
+    }
+  }
+}
+
+// Split schedule (SK == false): one segment per block.  Blocks are dealt to
+// the XCDs round-robin, so XCD x receives blocks x, x+8, ...; each XCD gets a
+// contiguous run of units, ordered (batch, head, key chunk, query block), so
+// the blocks resident on one XCD share a key chunk and read it from that
+// XCD's L2.
+//
+// Balanced schedule (SK == true): position p (XCD-contiguous) owns a
+// contiguous range of the (unit, tile) sequence, units ordered (batch, head,
+// query block).  A unit wholly inside the range is written directly; the
+// first and the last segment of the range may be pieces of units shared with
+// the neighbouring positions, written to partial slots 0 and 1 of p.
+template <bool SK>
+__global__ void __launch_bounds__(256, 3) attn_bf16_d64(AttnArgs a) {
+  // K tiles at stage*8 KB, V tiles at 24 KB + stage*8 KB.
+  __shared__ __attribute__((aligned(1024))) char lds[kStages * 2 * kTileBytes];
+  if constexpr (!SK) {
+    const int u = (blockIdx.x % kXcds) * a.units_per_xcd + blockIdx.x / kXcds;
+    if (u >= a.units) return;
+    const int qb = u % a.n_qblk;
+    int rest = u / a.n_qblk;
+    const int split = rest % a.n_split;
+    rest /= a.n_split;
+    const int h = rest % a.H;
+    const int b = rest / a.H;
+    const int t_begin = split * a.chunk_tiles;
+    const int t_end = min(a.n_tiles, t_begin + a.chunk_tiles);
+    attn_segment<false>(a, lds, b, h, qb, t_begin, t_end, split);
+  } else {
+    const long long p = static_cast<long long>(blockIdx.x % kXcds) * (a.sk_grid / kXcds) + blockIdx.x / kXcds;
+    const long long w0 = sk_start(p, a.work, a.sk_grid), w1 = sk_start(p + 1, a.work, a.sk_grid);
+    for (long long w = w0; w < w1;) {
+      const int u = static_cast<int>(w / a.n_tiles);
+      const int t_begin = static_cast<int>(w - static_cast<long long>(u) * a.n_tiles);
+      const int t_end = static_cast<int>(min(static_cast<long long>(a.n_tiles), t_begin + (w1 - w)));
+      const int qb = u % a.n_qblk;
+      const int h = (u / a.n_qblk) % a.H;
+      const int b = u / a.n_qblk / a.H;
+      const bool whole = t_begin == 0 && t_end == a.n_tiles;
+      if (w != w0) {
+        // the previous segment's LDS reads and stores are complete before
+        // this segment's loads refill the ring
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+      }
+      attn_segment<true>(a, lds, b, h, qb, t_begin, t_end, whole ? -1 : p * 2 + (w == w0 ? 0 : 1));
+      w += t_end - t_begin;
     }
   }
 }
@@ -459,8 +530,60 @@ attn_combine(const float* __restrict__ part_o, const float* __restrict__ part_ml
 
 struct AttnPlan {
   int n_qblk, n_tiles, n_split, chunk_tiles, units, units_per_xcd, grid;
+  int sk;
+  long long work;
   size_t ws_bytes;
 };
+
+// Merges the pieces of the units that the balanced schedule split between
+// positions.  One thread per (batch, query, head, 8-channel group); a unit
+// owned wholly by one position was written directly and is skipped.
+__global__ void __launch_bounds__(256)
+attn_combine_sk(const float* __restrict__ part_o, const float* __restrict__ part_ml, bf16_t* __restrict__ out,
+                int B, int H, int Tq, int n_qblk, int n_tiles, long long work, int grid) {
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int64_t total = static_cast<int64_t>(B) * Tq * H * 8;
+  if (idx >= total) return;
+  const int ch = static_cast<int>(idx & 7);
+  int64_t r = idx >> 3;
+  const int h = static_cast<int>(r % H);
+  r /= H;
+  const int q = static_cast<int>(r % Tq);
+  const int b = static_cast<int>(r / Tq);
+  const int qb = q / kBMq, row = q - qb * kBMq;
+  const long long u = (static_cast<long long>(b) * H + h) * n_qblk + qb;
+  const long long wf = u * n_tiles, wl = wf + n_tiles - 1;
+  const long long p0 = sk_owner(wf, work, grid), p1 = sk_owner(wl, work, grid);
+  if (p0 == p1) return;
+  float M = -INFINITY;
+  for (long long p = p0; p <= p1; ++p) {
+    if (sk_start(p + 1, work, grid) == sk_start(p, work, grid)) continue;  // empty range
+    const long long slot = p * 2 + (p == p0 && sk_start(p, work, grid) < wf ? 1 : 0);
+    M = fmaxf(M, part_ml[(slot * kBMq + row) * 2]);
+  }
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float L = 0.f;
+  for (long long p = p0; p <= p1; ++p) {
+    if (sk_start(p + 1, work, grid) == sk_start(p, work, grid)) continue;
+    const long long slot = p * 2 + (p == p0 && sk_start(p, work, grid) < wf ? 1 : 0);
+    const float* ml = part_ml + (slot * kBMq + row) * 2;
+    const float w = __builtin_amdgcn_exp2f(ml[0] - M);
+    L = fmaf(w, ml[1], L);
+    const float* po = part_o + (slot * kBMq + row) * kD + ch * 8;
+    const f32x4 x0 = *reinterpret_cast<const f32x4*>(po);
+    const f32x4 x1 = *reinterpret_cast<const f32x4*>(po + 4);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      acc[j] = fmaf(w, x0[j], acc[j]);
+      acc[4 + j] = fmaf(w, x1[j], acc[4 + j]);
+    }
+  }
+  const float inv = 1.0f / L;
+  u32x4 pk;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) pk[j] = pack_bf16x2(acc[2 * j] * inv, acc[2 * j + 1] * inv);
+  *reinterpret_cast<u32x4*>(out + (static_cast<int64_t>(b) * Tq + q) * H * kD + h * kD + ch * 8) = pk;
+}
 
 int device_cus() {
   static thread_local int cached_dev = -1, cached_cus = 256;
@@ -481,11 +604,12 @@ int device_cus() {
 }
 
 // Resident attention blocks per CU (registers and LDS), asked of the runtime.
+template <bool SK>
 int blocks_per_cu() {
   static thread_local int cached = 0;
   if (cached == 0) {
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_bf16_d64, 256, 0) != hipSuccess || n <= 0) {
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_bf16_d64<SK>, 256, 0) != hipSuccess || n <= 0) {
       (void)hipGetLastError();
       n = 2;
     }
@@ -494,15 +618,17 @@ int blocks_per_cu() {
   return cached;
 }
 
-// Picks the number of key chunks: each block runs one (batch, head, chunk,
-// query block) unit and the XCDs receive equal contiguous runs of units; the
-// estimated time is (rounds of resident blocks per XCD) x (tiles per unit),
-// plus the cost of the extra partial-output traffic when the keys are split.
+// Picks the schedule.  Split schedule: the number of key chunks; each block
+// runs one (batch, head, chunk, query block) unit and the XCDs receive equal
+// contiguous runs of units; the estimated time is (rounds of resident blocks
+// per XCD) x (tiles per unit), plus the cost of the extra partial-output
+// traffic when the keys are split.  The balanced schedule is priced the same
+// way: tiles per resident block plus its partial traffic.
 AttnPlan plan_attention(int64_t B, int64_t H, int64_t Tq, int64_t Tkv) {
   AttnPlan p{};
   p.n_qblk = static_cast<int>((Tq + kBMq - 1) / kBMq);
   p.n_tiles = static_cast<int>((Tkv + kBNk - 1) / kBNk);
-  const int slots_per_xcd = std::max(1, device_cus() / kXcds) * blocks_per_cu();
+  const int slots_per_xcd = std::max(1, device_cus() / kXcds) * blocks_per_cu<false>();
   const double base_units = static_cast<double>(B) * H * p.n_qblk;
   // cost unit: one 64-key tile of one block (~1 us); the split's partial
   // outputs cost their bytes at ~5 TB/s, i.e. ~5 MB per unit
@@ -523,6 +649,37 @@ AttnPlan plan_attention(int64_t B, int64_t H, int64_t Tq, int64_t Tkv) {
       best = cost;
       p.n_split = s_eff;
       p.chunk_tiles = chunk;
+    }
+  }
+  // Balanced schedule: one block per resident slot, each owning an equal
+  // contiguous share of the (unit, tile) sequence; at most two partial pieces
+  // per block go through the combine.  Blocks then read their keys at
+  // staggered offsets instead of in step with the other query blocks of their
+  // (batch, head), so their L2 reuse is lower: taken only where the K/V
+  // buffers fit well inside the last-level cache (half of its 256 MB) and the
+  // estimate beats the split schedule by 3%.  DP_ATTN_SCHEDULE=split or
+  // =balanced in the environment overrides the choice (for tests and tuning;
+  // the workspace query and the call must see the same setting).
+  {
+    const int slots = std::max(1, device_cus() / kXcds) * blocks_per_cu<true>() * kXcds;
+    const long long work = static_cast<long long>(base_units) * p.n_tiles;
+    const double per_slot = std::ceil(static_cast<double>(work) / slots);
+    const double sk_cost = per_slot + 2.0 * tile_cost +
+                           (2.0 * slots * kBMq * kD * 8.0 + 2.0 * B * Tq * H * kD) / bytes_per_tile_cost;
+    const double kv_bytes = 2.0 * B * Tkv * H * kD * 2;
+    const char* env = getenv("DP_ATTN_SCHEDULE");
+    const bool force_sk = env && strcmp(env, "balanced") == 0;
+    const bool force_split = env && strcmp(env, "split") == 0;
+    if (!force_split && (force_sk || (sk_cost < best * 0.97 && kv_bytes <= 128.0e6))) {
+      p.sk = 1;
+      p.work = work;
+      p.n_split = 1;
+      p.chunk_tiles = p.n_tiles;
+      p.units = static_cast<int>(base_units);
+      p.units_per_xcd = 0;
+      p.grid = slots;
+      p.ws_bytes = static_cast<size_t>(slots) * 2 * (kBMq * kD + kBMq * 2) * sizeof(float);
+      return p;
     }
   }
   p.units = static_cast<int>(base_units) * p.n_split;
@@ -649,8 +806,22 @@ DP_API dp_status dp_attn_stale_kv(const void* q, const void* k_buf, const void* 
     args.n_tiles = p.n_tiles;
     args.units = p.units;
     args.units_per_xcd = p.units_per_xcd;
-    hipLaunchKernelGGL(attn_bf16_d64, dim3(static_cast<unsigned>(p.grid)), dim3(256), 0, stream, args);
-    if (p.n_split > 1) {
+    args.sk = p.sk;
+    args.sk_grid = p.grid;
+    args.work = p.work;
+    if (p.sk) {
+      args.part_ml = args.part_o + static_cast<size_t>(p.grid) * 2 * kBMq * kD;
+    }
+    if (p.sk)
+      hipLaunchKernelGGL(attn_bf16_d64<true>, dim3(static_cast<unsigned>(p.grid)), dim3(256), 0, stream, args);
+    else
+      hipLaunchKernelGGL(attn_bf16_d64<false>, dim3(static_cast<unsigned>(p.grid)), dim3(256), 0, stream, args);
+    if (p.sk) {
+      const int64_t threads = B * Tq * H * 8;
+      hipLaunchKernelGGL(attn_combine_sk, dim3(static_cast<unsigned>((threads + 255) / 256)), dim3(256), 0,
+                         stream, args.part_o, args.part_ml, args.out, (int)B, (int)H, (int)Tq, p.n_qblk,
+                         p.n_tiles, p.work, p.grid);
+    } else if (p.n_split > 1) {
       const int64_t threads = B * Tq * H * 8;
       hipLaunchKernelGGL(attn_combine, dim3(static_cast<unsigned>((threads + 255) / 256)), dim3(256), 0,
                          stream, args.part_o, args.part_ml, args.out, (int)B, (int)H, (int)Tq, p.n_split);

@@ -89,7 +89,11 @@ dp_status dp_kv_buffer_splice(void* k_buf, void* v_buf, const void* k_fresh, con
  * in bf16 the probabilities are rounded to bf16 before the P*V product.
  * Supported: bf16 with d = 64; f32 with d in {32, 64}.
  * ws/ws_bytes: caller-owned device scratch of at least
- * dp_attn_stale_kv_workspace(...) bytes (NULL allowed when that is 0).
+ * dp_attn_stale_kv_workspace(...) bytes (NULL allowed when that is 0).  The
+ * size depends on the work schedule the library picks for the shape (and on
+ * the device's CU count); DP_ATTN_SCHEDULE=split or =balanced in the
+ * environment overrides that pick, so the query and the call must run with
+ * the same setting.
  * Errors: INVALID_ARG for NULL pointers, sizes <= 0 or a workspace that is too
  * small; UNSUPPORTED for other d or dtype combinations.
  */

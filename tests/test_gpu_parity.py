@@ -5,6 +5,8 @@ and check sampled outputs the oracle computes one by one (or every output
 where the oracle is cheap).  Tolerances are in tests/util.py."""
 from __future__ import annotations
 
+import contextlib
+import os
 import sys
 
 import numpy as np
@@ -23,6 +25,24 @@ R = synth.random_tensor
 
 def say(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+@contextlib.contextmanager
+def attn_schedule(name):
+    """Forces the bf16 attention's work schedule ("split" or "balanced"; None
+    leaves the pick to the library) for the workspace query and the call."""
+    old = os.environ.get("DP_ATTN_SCHEDULE")
+    if name is None:
+        os.environ.pop("DP_ATTN_SCHEDULE", None)
+    else:
+        os.environ["DP_ATTN_SCHEDULE"] = name
+    try:
+        yield
+    finally:
+        if old is None:
+            os.environ.pop("DP_ATTN_SCHEDULE", None)
+        else:
+            os.environ["DP_ATTN_SCHEDULE"] = old
 
 
 # --------------------------------------------------------------------- splice
@@ -150,31 +170,38 @@ def test_groupnorm_single_patch_null_stale():
     ("bf16", 1, 2, 64, 257, 1000), ("f32", 2, 2, 32, 512, 1024), ("f32", 1, 3, 64, 100, 77),
     ("f32", 1, 1, 32, 3, 1),
 ])
-def test_attention(dt, B, H, d, Tq, Tkv):
-    say("attn", dt, B, H, d, Tq, Tkv)
+@pytest.mark.parametrize("schedule", [None, "balanced"])
+def test_attention(dt, B, H, d, Tq, Tkv, schedule):
+    if dt == "f32" and schedule is not None:
+        pytest.skip("the f32 path has one schedule")
+    say("attn", dt, B, H, d, Tq, Tkv, schedule)
     q = R(1, "at.q", (B, Tq, H * d), dt)
     k = R(1, "at.k", (B, Tkv, H * d), dt)
     v = R(1, "at.v", (B, Tkv, H * d), dt)
-    out = ops.dp_attn_stale_kv(dev(q, dt), dev(k, dt), dev(v, dt), H)
+    with attn_schedule(schedule):
+        out = ops.dp_attn_stale_kv(dev(q, dt), dev(k, dt), dev(v, dt), H)
     assert_close(host(out), oracle.attention(q, k, v, H), dt, "attention")
 
 
 @pytest.mark.parametrize("Tq,Tkv,qscale", [(130, 700, 3.0), (70, 3001, 4.0), (64, 6000, 2.0), (33, 129, 4.0)])
-def test_attention_peaked_scores_bf16(Tq, Tkv, qscale):
+@pytest.mark.parametrize("schedule", [None, "balanced"])
+def test_attention_peaked_scores_bf16(Tq, Tkv, qscale, schedule):
     """Large-magnitude queries: softmax close to one-hot, so later key blocks
     can exceed the first block's max by far and force the reference to move
     (the 6000-key case also splits the key range across blocks)."""
-    say("attn peaked", Tq, Tkv, qscale)
+    say("attn peaked", Tq, Tkv, qscale, schedule)
     B, H, d = 1, 2, 64
     q = R(5, "atp.q", (B, Tq, H * d), "bf16", qscale)
     k = R(5, "atp.k", (B, Tkv, H * d), "bf16", 1.0)
     v = R(5, "atp.v", (B, Tkv, H * d), "bf16", 1.0)
-    out = ops.dp_attn_stale_kv(dev(q, "bf16"), dev(k, "bf16"), dev(v, "bf16"), H)
+    with attn_schedule(schedule):
+        out = ops.dp_attn_stale_kv(dev(q, "bf16"), dev(k, "bf16"), dev(v, "bf16"), H)
     assert_close(host(out), oracle.attention(q, k, v, H), "bf16", "attention peaked")
 
 
 @pytest.mark.parametrize("Tq,Tkv,hot", [(64, 300, (128, 192)), (32, 9000, (8500, 8600))])
-def test_attention_reference_moves(Tq, Tkv, hot):
+@pytest.mark.parametrize("schedule", [None, "balanced"])
+def test_attention_reference_moves(Tq, Tkv, hot, schedule):
     """A run of identical keys scoring ~69 (log2 units) above every earlier key:
     the kernel must move its softmax reference mid-sequence (rescaling the
     accumulated output, the row sums and the next block's scores already
@@ -191,8 +218,32 @@ def test_attention_reference_moves(Tq, Tkv, hot):
     v[:, hot[0]:hot[1]] = v[:, hot[0]]
     ref = oracle.attention(q, k, v, H)
     assert np.allclose(ref, np.broadcast_to(v[:, hot[0]][:, None, :], ref.shape), atol=1e-12)
-    out = ops.dp_attn_stale_kv(dev(q, "bf16"), dev(k, "bf16"), dev(v, "bf16"), H)
+    with attn_schedule(schedule):
+        out = ops.dp_attn_stale_kv(dev(q, "bf16"), dev(k, "bf16"), dev(v, "bf16"), H)
     assert_close(host(out), ref, "bf16", "attention reference moves")
+
+
+@pytest.mark.parametrize("B,H,Tq,Tkv", [
+    (1, 1, 128, 128000),   # one unit spread over every resident block: many pieces per unit
+    (2, 3, 129, 65),       # fewer (unit, tile) items than blocks: most blocks own nothing
+    (2, 10, 1024, 4096),   # SDXL-1024 64x64-level share: units and pieces mixed
+    (1, 4, 300, 2049),     # ragged queries and keys inside pieces
+])
+def test_attention_balanced_schedule(B, H, Tq, Tkv):
+    """The balanced schedule, forced on shapes that exercise its bookkeeping:
+    segments that start and end inside units, whole units written directly,
+    blocks with empty ranges, and the combine of every split unit; the split
+    schedule on the same inputs must agree with the oracle too."""
+    say("attn balanced", B, H, Tq, Tkv)
+    d = 64
+    q = R(8, "atb.q", (B, Tq, H * d), "bf16", 2.0)
+    k = R(8, "atb.k", (B, Tkv, H * d), "bf16")
+    v = R(8, "atb.v", (B, Tkv, H * d), "bf16")
+    ref = oracle.attention(q, k, v, H)
+    for sched in ("balanced", "split"):
+        with attn_schedule(sched):
+            out = ops.dp_attn_stale_kv(dev(q, "bf16"), dev(k, "bf16"), dev(v, "bf16"), H)
+        assert_close(host(out), ref, "bf16", f"attention, {sched} schedule")
 
 
 # ---------------------------------------------------------------- error paths
@@ -244,15 +295,17 @@ def test_groupnorm_max_channels(dt):
 
 
 @pytest.mark.parametrize("Tq,Tkv", [(1, 20000), (1000, 65), (3, 64)])
-def test_attention_degenerate_bf16(Tq, Tkv):
+@pytest.mark.parametrize("schedule", [None, "balanced"])
+def test_attention_degenerate_bf16(Tq, Tkv, schedule):
     """One query against a long (split) key range; many queries against one
     full tile plus one ragged key; fewer queries than one wave's group."""
-    say("attn degenerate", Tq, Tkv)
+    say("attn degenerate", Tq, Tkv, schedule)
     B, H, d = 1, 2, 64
     q = R(7, "atd.q", (B, Tq, H * d), "bf16")
     k = R(7, "atd.k", (B, Tkv, H * d), "bf16")
     v = R(7, "atd.v", (B, Tkv, H * d), "bf16")
-    out = ops.dp_attn_stale_kv(dev(q, "bf16"), dev(k, "bf16"), dev(v, "bf16"), H)
+    with attn_schedule(schedule):
+        out = ops.dp_attn_stale_kv(dev(q, "bf16"), dev(k, "bf16"), dev(v, "bf16"), H)
     assert_close(host(out), oracle.attention(q, k, v, H), "bf16", "attention degenerate")
 
 
