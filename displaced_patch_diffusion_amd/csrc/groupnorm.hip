@@ -174,27 +174,30 @@ __device__ void block_group_sums(const float* s1, const float* s2, bool active, 
 }
 
 // Folds the tile partials of batch item b into lane sums red[q*G + g] (lane q
-// takes tiles q, q + lanes, ..., in U interleaved accumulators so that U loads
-// are in flight); returns the lane count.  One fixed order, so every block
+// takes tiles q, q + lanes, ..., U per pass in U accumulators); returns the
+// lane count.  A pass issues all U loads before it adds any of them (indexes
+// past the last tile re-read that tile and are not added), so one memory
+// round trip covers up to U * lanes tiles.  One fixed order, so every block
 // (and dp_groupnorm_sums) derives bit-identical sums.
 __device__ int fold_partials(const GnArgs& a, int b, float2* red) {
   const int G = a.G;
   const int lanes = G >= kThreads ? 1 : kThreads / G;
   const float2* pb = a.partial + static_cast<int64_t>(b) * a.tiles * G;
-  constexpr int U = 8;  // independent loads in flight per thread
+  constexpr int U = 16;
   for (int f = threadIdx.x; f < lanes * G; f += kThreads) {
     const int g = f % G, q = f / G;
     float2 acc[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) acc[u] = make_float2(0.f, 0.f);
     for (int t0 = q; t0 < a.tiles; t0 += U * lanes) {
+      float2 v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) v[u] = pb[static_cast<int64_t>(min(t0 + u * lanes, a.tiles - 1)) * G + g];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const int t = t0 + u * lanes;
-        if (t < a.tiles) {
-          const float2 p = pb[static_cast<int64_t>(t) * G + g];
-          acc[u].x += p.x;
-          acc[u].y += p.y;
+        if (t0 + u * lanes < a.tiles) {
+          acc[u].x += v[u].x;
+          acc[u].y += v[u].y;
         }
       }
     }
@@ -209,11 +212,34 @@ __device__ int fold_partials(const GnArgs& a, int b, float2* red) {
   return lanes;
 }
 
+// The first kStalePre patches' stale sums of group g of batch item b, loaded
+// ahead of the fold so that their latency overlaps it (the thread of group g
+// finalises that group).
+constexpr int kStalePre = 8;
+struct StalePre {
+  float2 v[kStalePre];
+};
+
+__device__ __forceinline__ StalePre prefetch_stale(const GnArgs& a, int b, int g) {
+  StalePre sp;
+#pragma unroll
+  for (int j = 0; j < kStalePre; ++j) sp.v[j] = make_float2(0.f, 0.f);
+  if (g < a.G && a.n_patches > 1) {
+#pragma unroll
+    for (int j = 0; j < kStalePre; ++j) {
+      const float* st = a.stale + ((static_cast<int64_t>(min(j, a.n_patches - 1)) * a.B + b) * a.G + g) * 2;
+      sp.v[j] = make_float2(st[0], st[1]);
+    }
+  }
+  return sp;
+}
+
 // Statistics of batch item b from the lane sums red[q*G + g] (lanes in
 // order): fresh local sums out (tile 0 only), stale sums of the other
-// patches added, (mean, rstd) per group into gstat.
+// patches added in patch order (the first kStalePre from `pre`, prefetched by
+// the thread of group g = threadIdx.x), (mean, rstd) per group into gstat.
 __device__ void finalize_stats(const GnArgs& a, int b, int tile, int lanes, const float2* red,
-                               float2* gstat) {
+                               const StalePre& pre, float2* gstat) {
   const int G = a.G;
   for (int g = threadIdx.x; g < G; g += kThreads) {
     float f1 = 0.f, f2 = 0.f;
@@ -225,7 +251,16 @@ __device__ void finalize_stats(const GnArgs& a, int b, int tile, int lanes, cons
       a.fresh[(static_cast<int64_t>(b) * G + g) * 2 + 0] = f1;
       a.fresh[(static_cast<int64_t>(b) * G + g) * 2 + 1] = f2;
     }
-    for (int p = 0; p < a.n_patches; ++p) {
+    if (g == static_cast<int>(threadIdx.x)) {
+#pragma unroll
+      for (int j = 0; j < kStalePre; ++j) {
+        if (j < a.n_patches && j != a.rank) {
+          f1 += pre.v[j].x;
+          f2 += pre.v[j].y;
+        }
+      }
+    }
+    for (int p = g == static_cast<int>(threadIdx.x) ? kStalePre : 0; p < a.n_patches; ++p) {
       if (p == a.rank) continue;
       const float* st = a.stale + ((static_cast<int64_t>(p) * a.B + b) * G + g) * 2;
       f1 += st[0];
@@ -320,6 +355,7 @@ __global__ void __launch_bounds__(kThreads) gn_apply(GnArgs a) {
   for (int u = 0; u < kUnroll; ++u)
     first[u] = load_or_zero<BF16>(a, b, t_begin + tl + u * tpp, t_end, vi, active && u < npass);
 
+  const StalePre pre = prefetch_stale(a, b, tid);
   int lanes = 1;
   if (a.given) {  // the local sums come from the caller: one lane holding them
     for (int g = tid; g < G; g += kThreads)
@@ -328,7 +364,7 @@ __global__ void __launch_bounds__(kThreads) gn_apply(GnArgs a) {
     lanes = fold_partials(a, b, red);
   }
   __syncthreads();
-  finalize_stats(a, b, tile, lanes, red, gstat);
+  finalize_stats(a, b, tile, lanes, red, pre, gstat);
   __syncthreads();
 
   if (!active) return;
