@@ -33,10 +33,12 @@
 // Schedules.  A unit is (batch, head, 128-query block) against all keys.  The
 // split schedule gives each block one unit, or one of S equal key chunks of
 // it (partials merged by attn_combine), with the blocks of one key chunk
-// resident together on one XCD.  When the units do not fill whole rounds of
-// resident blocks, the balanced schedule gives each resident block an equal
-// contiguous range of the (unit, key tile) sequence; attn_combine_sk merges
-// the pieces of the units that neighbouring blocks share.
+// resident together on one XCD; when the units fill whole rounds of resident
+// blocks and leave a remainder, the full rounds may run whole and only the
+// remainder split.  When the units do not fill whole rounds, the balanced
+// schedule gives each resident block an equal contiguous range of the
+// (unit, key tile) sequence; attn_combine_sk merges the pieces of the units
+// that neighbouring blocks share.
 //
 // f32 (d = 32 or 64)
 // ------------------
@@ -81,6 +83,7 @@ struct AttnArgs {
   int B, H, Tq, Tkv;
   float c;          // scale * log2(e)
   int n_qblk, n_split, chunk_tiles, n_tiles, units, units_per_xcd;
+  int n_whole;      // split schedule: units 0..n_whole-1 run whole in the first blocks
   int sk;           // 1: balanced contiguous work ranges per block (see attn_bf16_d64)
   int sk_grid;      // blocks of the balanced schedule (a multiple of kXcds)
   long long work;   // units * n_tiles (balanced schedule)
@@ -400,7 +403,7 @@ __device__ __forceinline__ void attn_segment(const AttnArgs& a, char* lds, int b
 
   const float l_tot = swap_sum(l_part);
   if (!q_ok) return;
-  if (SK ? piece < 0 : a.n_split == 1) {
+  if (piece < 0) {
     const float inv = 1.0f / l_tot;
     bf16_t* op = a.out + (static_cast<int64_t>(b) * a.Tq + qi) * C + h * kD;
 #pragma unroll
@@ -442,7 +445,8 @@ __device__ __forceinline__ void attn_segment(const AttnArgs& a, char* lds, int b
 // the XCDs round-robin, so XCD x receives blocks x, x+8, ...; each XCD gets a
 // contiguous run of units, ordered (batch, head, key chunk, query block), so
 // the blocks resident on one XCD share a key chunk and read it from that
-// XCD's L2.
+// XCD's L2.  The first n_whole blocks (whole rounds, a multiple of 8) run
+// units 0..n_whole-1 whole; the key chunks of the other units follow.
 //
 // Balanced schedule (SK == true): position p (XCD-contiguous) owns a
 // contiguous range of the (unit, tile) sequence, units ordered (batch, head,
@@ -454,17 +458,34 @@ __global__ void __launch_bounds__(256, 3) attn_bf16_d64(AttnArgs a) {
   // K tiles at stage*8 KB, V tiles at 24 KB + stage*8 KB.
   __shared__ __attribute__((aligned(1024))) char lds[kStages * 2 * kTileBytes];
   if constexpr (!SK) {
-    const int u = (blockIdx.x % kXcds) * a.units_per_xcd + blockIdx.x / kXcds;
-    if (u >= a.units) return;
-    const int qb = u % a.n_qblk;
-    int rest = u / a.n_qblk;
-    const int split = rest % a.n_split;
-    rest /= a.n_split;
-    const int h = rest % a.H;
-    const int b = rest / a.H;
+    if (static_cast<int>(blockIdx.x) < a.n_whole) {
+      // first round: whole units, n_whole / 8 consecutive ones per XCD
+      const int u = (blockIdx.x % kXcds) * (a.n_whole / kXcds) + blockIdx.x / kXcds;
+      attn_segment<false>(a, lds, u / a.n_qblk / a.H, (u / a.n_qblk) % a.H, u % a.n_qblk, 0, a.n_tiles, -1);
+      return;
+    }
+    // the key chunks of the remaining units, ordered (batch, head, chunk,
+    // query block); the first (batch, head) may start part-way through its
+    // query blocks
+    const int i = blockIdx.x - a.n_whole;
+    const int k = (i % kXcds) * a.units_per_xcd + i / kXcds;
+    if (k >= a.units) return;
+    const int nq = a.n_qblk, S = a.n_split;
+    const int g0 = a.n_whole / nq, off0 = a.n_whole - g0 * nq, n0 = nq - off0;
+    int g, split, qb;
+    if (k < n0 * S) {
+      g = g0;
+      split = k / n0;
+      qb = off0 + k % n0;
+    } else {
+      const int r = k - n0 * S;
+      g = g0 + 1 + r / (nq * S);
+      split = (r % (nq * S)) / nq;
+      qb = r % nq;
+    }
     const int t_begin = split * a.chunk_tiles;
     const int t_end = min(a.n_tiles, t_begin + a.chunk_tiles);
-    attn_segment<false>(a, lds, b, h, qb, t_begin, t_end, split);
+    attn_segment<false>(a, lds, g / a.H, g % a.H, qb, t_begin, t_end, S == 1 ? -1 : split);
   } else {
     const long long p = static_cast<long long>(blockIdx.x % kXcds) * (a.sk_grid / kXcds) + blockIdx.x / kXcds;
     const long long w0 = sk_start(p, a.work, a.sk_grid), w1 = sk_start(p + 1, a.work, a.sk_grid);
@@ -492,7 +513,7 @@ __global__ void __launch_bounds__(256, 3) attn_bf16_d64(AttnArgs a) {
 // One thread per (batch, query, head, 8-channel group).
 __global__ void __launch_bounds__(256)
 attn_combine(const float* __restrict__ part_o, const float* __restrict__ part_ml,
-             bf16_t* __restrict__ out, int B, int H, int Tq, int S) {
+             bf16_t* __restrict__ out, int B, int H, int Tq, int S, int n_whole) {
   const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   const int64_t total = static_cast<int64_t>(B) * Tq * H * 8;
   if (idx >= total) return;
@@ -502,6 +523,7 @@ attn_combine(const float* __restrict__ part_o, const float* __restrict__ part_ml
   r /= H;
   const int q = static_cast<int>(r % Tq);
   const int b = static_cast<int>(r / Tq);
+  if ((static_cast<int64_t>(b) * H + h) * ((Tq + kBMq - 1) / kBMq) + q / kBMq < n_whole) return;  // written whole
   const int C = H * kD;
   float M = -INFINITY;
   for (int s = 0; s < S; ++s)
@@ -530,6 +552,7 @@ attn_combine(const float* __restrict__ part_o, const float* __restrict__ part_ml
 
 struct AttnPlan {
   int n_qblk, n_tiles, n_split, chunk_tiles, units, units_per_xcd, grid;
+  int n_whole;
   int sk;
   long long work;
   size_t ws_bytes;
@@ -634,21 +657,31 @@ AttnPlan plan_attention(int64_t B, int64_t H, int64_t Tq, int64_t Tkv) {
   // outputs cost their bytes at ~5 TB/s, i.e. ~5 MB per unit
   const double tile_cost = 1.0;
   const double bytes_per_tile_cost = 5.0e6;
+  // The split schedule may run the units of its full rounds whole (n_whole
+  // of them, the first blocks) and split only the rest: the same rounds, but
+  // partial outputs for the last round's units alone.
+  const int slots = slots_per_xcd * kXcds;
+  const int whole_max = static_cast<int>(base_units) / slots * slots;
   double best = 1e300;
   for (int S = 1; S <= 16 && S <= p.n_tiles; ++S) {
     const int chunk = (p.n_tiles + S - 1) / S;
     const int s_eff = (p.n_tiles + chunk - 1) / chunk;
     if (s_eff != S && S > 1) continue;
-    const double units = base_units * s_eff;
-    const double per_xcd = std::ceil(units / kXcds);
-    const double rounds = std::ceil(per_xcd / slots_per_xcd);
-    double cost = rounds * chunk * tile_cost;
-    if (s_eff > 1)
-      cost += (static_cast<double>(s_eff) * 8.0 + 2.0) * B * Tq * H * kD / bytes_per_tile_cost;
-    if (cost < best * 0.999) {
-      best = cost;
-      p.n_split = s_eff;
-      p.chunk_tiles = chunk;
+    for (int whole : {0, whole_max}) {
+      if (whole > 0 && (s_eff == 1 || whole == static_cast<int>(base_units))) continue;
+      const double rest = base_units - whole;
+      const double per_xcd = std::ceil(rest * s_eff / kXcds);
+      const double rounds = static_cast<double>(whole) / slots + std::ceil(per_xcd / slots_per_xcd) * chunk /
+                                                                      static_cast<double>(p.n_tiles);
+      double cost = rounds * p.n_tiles * tile_cost;
+      if (s_eff > 1)
+        cost += (static_cast<double>(s_eff) * 8.0 + 2.0) * (rest / base_units) * B * Tq * H * kD / bytes_per_tile_cost;
+      if (cost < best * 0.999) {
+        best = cost;
+        p.n_split = s_eff;
+        p.chunk_tiles = chunk;
+        p.n_whole = whole;
+      }
     }
   }
   // Balanced schedule: one block per resident slot, each owning an equal
@@ -661,11 +694,11 @@ AttnPlan plan_attention(int64_t B, int64_t H, int64_t Tq, int64_t Tkv) {
   // =balanced in the environment overrides the choice (for tests and tuning;
   // the workspace query and the call must see the same setting).
   {
-    const int slots = std::max(1, device_cus() / kXcds) * blocks_per_cu<true>() * kXcds;
+    const int sk_slots = std::max(1, device_cus() / kXcds) * blocks_per_cu<true>() * kXcds;
     const long long work = static_cast<long long>(base_units) * p.n_tiles;
-    const double per_slot = std::ceil(static_cast<double>(work) / slots);
+    const double per_slot = std::ceil(static_cast<double>(work) / sk_slots);
     const double sk_cost = per_slot + 2.0 * tile_cost +
-                           (2.0 * slots * kBMq * kD * 8.0 + 2.0 * B * Tq * H * kD) / bytes_per_tile_cost;
+                           (2.0 * sk_slots * kBMq * kD * 8.0 + 2.0 * B * Tq * H * kD) / bytes_per_tile_cost;
     const double kv_bytes = 2.0 * B * Tkv * H * kD * 2;
     const char* env = getenv("DP_ATTN_SCHEDULE");
     const bool force_sk = env && strcmp(env, "balanced") == 0;
@@ -675,16 +708,17 @@ AttnPlan plan_attention(int64_t B, int64_t H, int64_t Tq, int64_t Tkv) {
       p.work = work;
       p.n_split = 1;
       p.chunk_tiles = p.n_tiles;
+      p.n_whole = 0;
       p.units = static_cast<int>(base_units);
       p.units_per_xcd = 0;
-      p.grid = slots;
-      p.ws_bytes = static_cast<size_t>(slots) * 2 * (kBMq * kD + kBMq * 2) * sizeof(float);
+      p.grid = sk_slots;
+      p.ws_bytes = static_cast<size_t>(sk_slots) * 2 * (kBMq * kD + kBMq * 2) * sizeof(float);
       return p;
     }
   }
-  p.units = static_cast<int>(base_units) * p.n_split;
+  p.units = (static_cast<int>(base_units) - p.n_whole) * p.n_split;
   p.units_per_xcd = (p.units + kXcds - 1) / kXcds;
-  p.grid = p.units_per_xcd * kXcds;
+  p.grid = p.n_whole + p.units_per_xcd * kXcds;
   p.ws_bytes = p.n_split > 1 ? static_cast<size_t>(p.n_split) * B * Tq * H * kD * sizeof(float) +
                                    static_cast<size_t>(p.n_split) * B * H * Tq * 2 * sizeof(float)
                              : 0;
@@ -806,6 +840,7 @@ DP_API dp_status dp_attn_stale_kv(const void* q, const void* k_buf, const void* 
     args.n_tiles = p.n_tiles;
     args.units = p.units;
     args.units_per_xcd = p.units_per_xcd;
+    args.n_whole = p.n_whole;
     args.sk = p.sk;
     args.sk_grid = p.grid;
     args.work = p.work;
@@ -824,7 +859,8 @@ DP_API dp_status dp_attn_stale_kv(const void* q, const void* k_buf, const void* 
     } else if (p.n_split > 1) {
       const int64_t threads = B * Tq * H * 8;
       hipLaunchKernelGGL(attn_combine, dim3(static_cast<unsigned>((threads + 255) / 256)), dim3(256), 0,
-                         stream, args.part_o, args.part_ml, args.out, (int)B, (int)H, (int)Tq, p.n_split);
+                         stream, args.part_o, args.part_ml, args.out, (int)B, (int)H, (int)Tq, p.n_split,
+                         p.n_whole);
     }
   } else {
     const dim3 grid(static_cast<unsigned>((Tq + kFQ - 1) / kFQ), static_cast<unsigned>(H),

@@ -246,6 +246,25 @@ def test_attention_balanced_schedule(B, H, Tq, Tkv):
         assert_close(host(out), ref, "bf16", f"attention, {sched} schedule")
 
 
+def test_attention_whole_rounds_then_split():
+    """The split schedule with its full rounds run whole and only the last
+    round's units split into key chunks (picked for 1000 query blocks on 768
+    slots): sampled query rows vs the oracle, from whole units, from split
+    units, and at the boundary between them inside one (batch, head)."""
+    B, H, Tq, Tkv, d = 2, 2, 32000, 2560, 64
+    say("attn whole rounds then split", B, H, Tq, Tkv)
+    q = R(9, "atw.q", (B, Tq, H * d), "bf16")
+    k = R(9, "atw.k", (B, Tkv, H * d), "bf16")
+    v = R(9, "atw.v", (B, Tkv, H * d), "bf16")
+    with attn_schedule("split"):
+        out = host(ops.dp_attn_stale_kv(dev(q, "bf16"), dev(k, "bf16"), dev(v, "bf16"), H))
+    # units are (batch, head, 128-query block); with 768 slots the first 768
+    # units (batch 0, and batch 1 head 0 plus 18 blocks of head 1) run whole
+    rows = np.array(sorted({0, 1, 127, 128, 16383, 17 * 128 - 1, 17 * 128, 18 * 128 - 1, 18 * 128,
+                            18 * 128 + 1, 19 * 128, 24000, Tq - 1}))
+    assert_close(out[:, rows], oracle.attention(q[:, rows], k, v, H), "bf16", "attention whole + split")
+
+
 # ---------------------------------------------------------------- error paths
 def test_errors_raise_before_launch():
     x = torch.zeros((4, 48), dtype=torch.bfloat16, device="cuda")
