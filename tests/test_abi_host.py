@@ -81,6 +81,38 @@ def test_attention_validation(lib):
     assert st == _lib.DP_ERR_INVALID_ARG and "overlap" in msg
 
 
+def _attn_ws(lib, schedule, B, H, Tq, Tkv):
+    old = os.environ.get("DP_ATTN_SCHEDULE")
+    if schedule is None:
+        os.environ.pop("DP_ATTN_SCHEDULE", None)
+    else:
+        os.environ["DP_ATTN_SCHEDULE"] = schedule
+    try:
+        return lib.dp_attn_stale_kv_workspace(B, H, Tq, Tkv, 64, _lib.DP_BF16)
+    finally:
+        if old is None:
+            os.environ.pop("DP_ATTN_SCHEDULE", None)
+        else:
+            os.environ["DP_ATTN_SCHEDULE"] = old
+
+
+def test_attention_workspace_follows_the_schedule(lib):
+    """The workspace is the chosen schedule's partial storage: none for a
+    single unsplit round; S key chunks of float32 rows plus (reference, sum)
+    pairs for a split; two 128-row pieces per resident block (a multiple of 8
+    blocks, whatever the shape) for the balanced schedule."""
+    assert _attn_ws(lib, "split", 1, 1, 128, 64) == 0
+    piece = 2 * (128 * 64 + 128 * 2) * 4
+    bal = [_attn_ws(lib, "balanced", *shp) for shp in ((1, 1, 128, 64), (2, 10, 7200, 57600), (1, 4, 300, 2049))]
+    assert bal[0] == bal[1] == bal[2] > 0 and bal[0] % (8 * piece) == 0
+    B, H, Tq = 2, 10, 7200
+    split = _attn_ws(lib, "split", B, H, Tq, 57600)
+    per_chunk = B * Tq * H * 64 * 4 + B * H * Tq * 2 * 4
+    assert split > 0 and split % per_chunk == 0 and split // per_chunk >= 2
+    # an unknown value leaves the pick to the library
+    assert _attn_ws(lib, "bogus", B, H, Tq, 57600) == _attn_ws(lib, None, B, H, Tq, 57600)
+
+
 def test_conv_and_linear_validation(lib):
     st, _ = status_and_error(lib.dp_conv3x3_stale_halo, A, None, None, Bp, None, Cp, 2, 4, 8, 48, 64,
                              _lib.DP_BF16, None)
