@@ -18,8 +18,9 @@ timing.
 Prints one JSON line.  value = algorithmic dense FLOPs of the step (attention
 + projections + convs) / measured step time, in TFLOP/s.  The K timed steps
 carry HIP events only around the attention call (its average duration gives
-roofline.achieved); the per-op breakdown under "kernels" comes from K further
-steps with an event after every op, since each event adds queue time.
+roofline.achieved); the per-op breakdown under "kernels" times each op
+enqueued K times back to back (every op is idempotent on its inputs), since an
+event between ops adds queue time.
 """
 from __future__ import annotations
 
@@ -179,66 +180,77 @@ class Share:
             self.conv_in_loc = None
         torch.cuda.synchronize()
 
-    # one step; `mark(name)` is called after each op is enqueued
-    def step(self, mark):
+    # the ops of one step, in order, as (name, enqueue function)
+    def op_list(self):
         w, ops = self.w, self.ops
         B = w.B
+        L = []
         if w.two_level:
             hc, Wc, Cc = self.hc, w.conv_W, w.conv_C
+            shp = (B, hc, Wc, Cc)
             x = self.conv_in_loc
             for i in range(2):
                 gi, ci = self.gns[i], self.convs[i]
+                gin, gout, zout, fr = x, self.gc[i], self.zc[i], self.fresh
                 if self.gn_sums_in_conv and i == 1:
-                    ops.dp_groupnorm_apply(x, self.fresh[1], gi["stale"], w.rank, w.conv_H * Wc, gi["gamma"],
-                                           gi["beta"], w.eps, True, self.G, y=self.gc[i])
+                    L.append(("groupnorm", lambda gi=gi, gin=gin, gout=gout, fr=fr: ops.dp_groupnorm_apply(
+                        gin, fr[1], gi["stale"], w.rank, w.conv_H * Wc, gi["gamma"], gi["beta"], w.eps, True,
+                        self.G, y=gout)))
                 else:
-                    ops.dp_groupnorm_stale_stats(x, gi["stale"], w.rank, w.conv_H * Wc, gi["gamma"],
-                                                 gi["beta"], w.eps, True, self.G, y=self.gc[i],
-                                                 fresh_sums_out=self.fresh[i], ws=self.gn_ws)
-                mark("groupnorm")
+                    L.append(("groupnorm", lambda gi=gi, gin=gin, gout=gout, fr=fr[i]: ops.dp_groupnorm_stale_stats(
+                        gin, gi["stale"], w.rank, w.conv_H * Wc, gi["gamma"], gi["beta"], w.eps, True, self.G,
+                        y=gout, fresh_sums_out=fr, ws=self.gn_ws)))
                 if self.gn_sums_in_conv and i == 0:
                     # the conv epilogue also forms the local sums the next GroupNorm needs
-                    ops.dp_conv3x3_stale_halo_gn_sums(self.gc[i].view(B, hc, Wc, Cc), ci["ht"], ci["hb"],
-                                                      ci["w"], ci["b"], self.G, y=self.zc[i].view(B, hc, Wc, Cc),
-                                                      gn_sums=self.fresh[1], ws=self.conv_ws)
+                    L.append(("conv", lambda ci=ci, gout=gout, zout=zout: ops.dp_conv3x3_stale_halo_gn_sums(
+                        gout.view(shp), ci["ht"], ci["hb"], ci["w"], ci["b"], self.G, y=zout.view(shp),
+                        gn_sums=self.fresh[1], ws=self.conv_ws)))
                 else:
-                    ops.dp_conv3x3_stale_halo(self.gc[i].view(B, hc, Wc, Cc), ci["ht"], ci["hb"], ci["w"],
-                                              ci["b"], y=self.zc[i].view(B, hc, Wc, Cc))
-                mark("conv")
-                x = self.zc[i]
+                    L.append(("conv", lambda ci=ci, gout=gout, zout=zout: ops.dp_conv3x3_stale_halo(
+                        gout.view(shp), ci["ht"], ci["hb"], ci["w"], ci["b"], y=zout.view(shp))))
+                x = zout
         if self.fused_qkv:
             # one launch: Q/K/V of the local rows, K and V written into the buffers
-            ops.dp_qkv_projection_into_buffers(self.x_loc, self.wq, self.wk, self.wv, self.k_buf,
-                                               self.v_buf, self.t0, q=self.q)
-            mark("proj")
+            L.append(("proj", lambda: ops.dp_qkv_projection_into_buffers(
+                self.x_loc, self.wq, self.wk, self.wv, self.k_buf, self.v_buf, self.t0, q=self.q)))
         else:
-            ops.dp_linear(self.x_loc, self.wq, y=self.q)
-            ops.dp_linear(self.x_loc, self.wk, y=self.kf)
-            ops.dp_linear(self.x_loc, self.wv, y=self.vf)
-            mark("proj")
-            ops.dp_kv_buffer_splice(self.k_buf, self.v_buf, self.kf, self.vf, self.t0)
-            mark("splice")
-        ops.dp_attn_stale_kv(self.q, self.k_buf, self.v_buf, w.heads, out=self.o, ws=self.attn_ws)
-        mark("attn")
-        ops.dp_linear(self.o, self.wo, y=self.y)
-        mark("proj")
+            def three():
+                ops.dp_linear(self.x_loc, self.wq, y=self.q)
+                ops.dp_linear(self.x_loc, self.wk, y=self.kf)
+                ops.dp_linear(self.x_loc, self.wv, y=self.vf)
+            L.append(("proj", three))
+            L.append(("splice", lambda: ops.dp_kv_buffer_splice(self.k_buf, self.v_buf, self.kf, self.vf,
+                                                                self.t0)))
+        L.append(("attn", lambda: ops.dp_attn_stale_kv(self.q, self.k_buf, self.v_buf, w.heads, out=self.o,
+                                                        ws=self.attn_ws)))
+        L.append(("proj", lambda: ops.dp_linear(self.o, self.wo, y=self.y)))
         if not w.two_level:
             c, g = self.convs[0], self.gns[0]
             shp = (B, self.hc, w.conv_W, w.conv_C)
             if self.gn_sums_in_conv:
                 # the conv epilogue forms the GroupNorm's local sums; the GroupNorm is one pass
-                ops.dp_conv3x3_stale_halo_gn_sums(self.y.view(shp), c["ht"], c["hb"], c["w"], c["b"], self.G,
-                                                  y=self.zc[0].view(shp), gn_sums=self.fresh[0], ws=self.conv_ws)
-                mark("conv")
-                ops.dp_groupnorm_apply(self.zc[0], self.fresh[0], g["stale"], w.rank, w.conv_H * w.conv_W,
-                                       g["gamma"], g["beta"], w.eps, False, self.G, y=self.gc[0])
+                L.append(("conv", lambda: ops.dp_conv3x3_stale_halo_gn_sums(
+                    self.y.view(shp), c["ht"], c["hb"], c["w"], c["b"], self.G, y=self.zc[0].view(shp),
+                    gn_sums=self.fresh[0], ws=self.conv_ws)))
+                L.append(("groupnorm", lambda: ops.dp_groupnorm_apply(
+                    self.zc[0], self.fresh[0], g["stale"], w.rank, w.conv_H * w.conv_W, g["gamma"], g["beta"],
+                    w.eps, False, self.G, y=self.gc[0])))
             else:
-                ops.dp_conv3x3_stale_halo(self.y.view(shp), c["ht"], c["hb"], c["w"], c["b"], y=self.zc[0].view(shp))
-                mark("conv")
-                ops.dp_groupnorm_stale_stats(self.zc[0], g["stale"], w.rank, w.conv_H * w.conv_W,
-                                             g["gamma"], g["beta"], w.eps, False, self.G, y=self.gc[0],
-                                             fresh_sums_out=self.fresh[0], ws=self.gn_ws)
-            mark("groupnorm")
+                L.append(("conv", lambda: ops.dp_conv3x3_stale_halo(
+                    self.y.view(shp), c["ht"], c["hb"], c["w"], c["b"], y=self.zc[0].view(shp))))
+                L.append(("groupnorm", lambda: ops.dp_groupnorm_stale_stats(
+                    self.zc[0], g["stale"], w.rank, w.conv_H * w.conv_W, g["gamma"], g["beta"], w.eps, False,
+                    self.G, y=self.gc[0], fresh_sums_out=self.fresh[0], ws=self.gn_ws)))
+        return L
+
+    # one step; `mark(name)` is called after each op is enqueued
+    def step(self, mark):
+        for name, fn in self.ops_:
+            fn()
+            mark(name)
+
+    def prepare(self):
+        self.ops_ = self.op_list()
 
 
 # ------------------------------------------------------------ OTIL transmit
@@ -498,6 +510,7 @@ def main():
     share = Share(w, torch, ops, synth)
     share.fused_qkv = args.qkv == "fused"
     share.gn_sums_in_conv = args.gn_sums == "conv"
+    share.prepare()
 
     names = []
 
@@ -505,12 +518,27 @@ def main():
         names.append(name)
 
     share.step(collect)
-    n_marks = len(names)
     for _ in range(args.warmup):
         share.step(lambda n: None)
     torch.cuda.synchronize()
 
     K = args.steps
+    # Per-op breakdown, before the timed steps: each op of the step enqueued K
+    # times back to back between two events, behind a GPU spin that lets the
+    # host queue them all, so neither event queue time nor host launch time
+    # enters the average.
+    per_op = {}
+    for name, fn in share.ops_:
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(2_000_000)
+        e0.record()
+        for _ in range(K):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        per_op[name] = per_op.get(name, 0.0) + e0.elapsed_time(e1) * 1e-3 / K
     # Timed region: K steps with HIP events only around the attention call (on
     # torch's current stream, where every library call launches); an event
     # between every op costs a few microseconds of queue time each.
@@ -536,25 +564,6 @@ def main():
     log(f"bench: {K} steps in {wall:.4f}s")
     attn_t = sum(a.elapsed_time(b) for a, b in att) * 1e-3 / K
 
-    # Per-op breakdown: K more steps with an event after every op.
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(n_marks + 1)] for _ in range(K)]
-    for s in range(K):
-        e = ev[s]
-        e[0].record()
-        idx = [0]
-
-        def mark(_name, e=e, idx=idx):
-            idx[0] += 1
-            e[idx[0]].record()
-
-        share.step(mark)
-    torch.cuda.synchronize()
-
-    per_op = {}
-    for s in range(K):
-        for i, name in enumerate(names):
-            per_op.setdefault(name, 0.0)
-            per_op[name] += ev[s][i].elapsed_time(ev[s][i + 1]) * 1e-3 / K
     per_op["attn"] = attn_t
     fl, by = w.flops(), w.bytes()
     step_s = wall / K
