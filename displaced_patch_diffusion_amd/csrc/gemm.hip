@@ -130,6 +130,7 @@ __global__ void __launch_bounds__(64 * NW, OCC) gemm_bf16(GemmArgs g) {
   constexpr int kQ = BK / 16;                              // 16-wide MFMA k steps per stage
   constexpr int WM = BM / WGM, WN = BN / WGN, MB = WM / 32, NB = WN / 32;
   static_assert(BK == 32 || BK == 64, "slice width");
+  static_assert(ST >= 2 && ST <= 4, "the k loop below unrolls at most four ring stages");
   static_assert(WGM * WGN == NW && WM % 32 == 0 && WN % 32 == 0 && BM % RPS == 0 && BN % RPS == 0, "tile");
   __shared__ __attribute__((aligned(1024))) char lds[ST * kStageBytes];
 
