@@ -409,6 +409,52 @@ def test_full_size_share(name):
     assert_close(host(yg), ref, dt, "groupnorm")
 
 
+@pytest.mark.parametrize("rank", [0, 7])
+def test_full_size_edge_ranks(rank):
+    """The SDXL-3840 share of the first and the last row band, at full size, in
+    the launch configuration the benchmark times: fused Q/K/V written into the
+    buffers at the band's first and last token range (sampled rows vs the
+    oracle; rows outside the band untouched), attention over that buffer, and
+    the conv whose missing halo is the image edge (zeros, NULL halo)."""
+    w = synth.WORKLOADS["sdxl3840_l240_c640"].with_rank(rank)
+    dt, B, C, Tq, Tkv, t0 = w.dtype, w.B, w.attn_C, w.Tq, w.T_kv, w.t0
+    say("full-size edge rank", rank, "t0", t0)
+    x = R(1, f"edge{rank}.x", (B, Tq, C), dt)
+    wq, wk, wv = (R(0, f"edge{rank}.w{n}", (C, C), dt, C ** -0.5) for n in "qkv")
+    kb, vb = R(1, f"edge{rank}.kb", (B, Tkv, C), dt), R(1, f"edge{rank}.vb", (B, Tkv, C), dt)
+    gk, gv = dev(kb, dt), dev(vb, dt)
+    q = ops.dp_qkv_projection_into_buffers(dev(x, dt), dev(wq, dt), dev(wk, dt), dev(wv, dt), gk, gv, t0)
+    rows = sample_rows(Tq, 8, 11 + rank)
+    assert_close(host(q)[:, rows], oracle.linear(x[:, rows], wq), dt, "q")
+    hk, hv = host(gk), host(gv)
+    assert_close(hk[:, t0 + rows], oracle.linear(x[:, rows], wk), dt, "k rows")
+    assert_close(hv[:, t0 + rows], oracle.linear(x[:, rows], wv), dt, "v rows")
+    outside = np.r_[0:t0, t0 + Tq:Tkv]
+    assert np.array_equal(hk[:, outside], kb[:, outside]) and np.array_equal(hv[:, outside], vb[:, outside])
+    # the oracle's buffers: its own projections, stored in the buffers' dtype
+    ek, ev = oracle.kv_buffer_splice(kb, vb, synth.as_storage(oracle.linear(x, wk), dt),
+                                     synth.as_storage(oracle.linear(x, wv), dt), t0)
+    del hk, hv
+    out = host(ops.dp_attn_stale_kv(q, gk, gv, w.heads))
+    del gk, gv
+    assert_close(out[:, rows], oracle.attention(oracle.linear(x[:, rows], wq), ek, ev, w.heads), dt,
+                 "attention")
+    # conv: the edge rows take zeros for the missing halo
+    Cc, h, Wd = w.conv_C, w.conv_h, w.conv_W
+    xc = R(1, f"edge{rank}.xc", (B, h, Wd, Cc), dt)
+    cw = R(0, f"edge{rank}.cw", (Cc, 3, 3, Cc), dt, (9 * Cc) ** -0.5)
+    halo = R(2, f"edge{rank}.halo", (B, Wd, Cc), dt)
+    ht, hb = (None, halo) if rank == 0 else (halo, None)
+    yc = host(ops.dp_conv3x3_stale_halo(dev(xc, dt), None if ht is None else dev(ht, dt),
+                                        None if hb is None else dev(hb, dt), dev(cw, dt), None))
+    for i in (0, h - 1):
+        top = xc[:, i - 1] if i > 0 else ht
+        bot = xc[:, i + 1] if i < h - 1 else hb
+        ref = oracle.conv3x3_halo(xc[:, i:i + 1], top, bot, cw, None)
+        cols = sample_rows(Wd, 24, i)
+        assert_close(yc[:, i:i + 1, cols], ref[:, :, cols], dt, f"conv row {i}")
+
+
 # ----------------------------------------------------------- whole fp32 chain
 def _share_inputs(w, rank):
     """Inputs of one rank's share for the single-level chain: stale K/V from
