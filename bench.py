@@ -253,6 +253,22 @@ class Share:
         self.ops_ = self.op_list()
 
 
+def back_to_back_us(torch, fn, reps: int) -> float:
+    """Average duration of `fn`'s launches, enqueued `reps` times back to back
+    between two events behind a GPU spin that lets the host queue them all (no
+    host launch latency and no per-call event inside the interval)."""
+    fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda._sleep(2_000_000)
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / reps
+
+
 # ------------------------------------------------------------ OTIL transmit
 def otil_timing(torch, ops, synth, steps: int):
     """OTIL selective transmit at the pages' setting (SDXL 1024^2, 4 ranks,
@@ -272,31 +288,17 @@ def otil_timing(torch, ops, synth, steps: int):
     packed = torch.empty((k, B, bh, bw, C), dtype=torch.float16, device="cuda")
     last0 = last.clone()
 
-    def send():
-        last.copy_(last0)  # same work every repetition: restore the last-sent state (not timed)
-        e0.record()
-        ops.dp_otil_select_pack(band, last, vis, bh, bw, k, scores=scores, idx=idx, packed=packed)
-        e1.record()
-        for p in (0, 2, 3):
-            ops.dp_otil_unpack(copy, packed, idx, p * h, h, bh, bw)
-        e2.record()
-
-    e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
-    for _ in range(5):
-        send()
-    torch.cuda.synchronize()
-    ts, tu = [], []
-    for _ in range(steps):
-        send()
-        torch.cuda.synchronize()
-        ts.append(e0.elapsed_time(e1) * 1e3)
-        tu.append(e1.elapsed_time(e2) * 1e3 / 3)
+    # Every select_pack call scores all K blocks and packs k of them, whatever
+    # the visited flags and last-sent state left by the call before, so the
+    # calls repeat the same work back to back; unpack copies k blocks.
+    t_s = back_to_back_us(torch, lambda: ops.dp_otil_select_pack(band, last, vis, bh, bw, k, scores=scores, idx=idx,
+                                                                 packed=packed), steps)
+    t_u = back_to_back_us(torch, lambda: ops.dp_otil_unpack(copy, packed, idx, 2 * h, h, bh, bw), steps)
     es = 2
     band_b = B * h * W * C * es
     blk_b = k * B * bh * bw * C * es
     send_bytes = 2 * band_b + 3 * blk_b    # score reads x, last_sent; pack reads k blocks, writes packed + last_sent
     unpack_bytes = 2 * blk_b               # per peer: read packed, write the blocks
-    t_s, t_u = float(np.median(ts)), float(np.median(tu))
     return {"workload": "SDXL 1024^2 latent band 32x128, C=4, batch 2, fp16, 8x8 blocks, K=64, k=32, 4 ranks",
             "select_pack_us": round(t_s, 2), "unpack_us_per_peer": round(t_u, 2),
             "select_pack_bytes": send_bytes, "unpack_bytes_per_peer": unpack_bytes,
@@ -309,7 +311,8 @@ def vae_rows_timing(torch, ops, synth, name: str, steps: int):
     """One rank's band of a KL-VAE decoder resnet in DistVAE's row mode: group
     sums, GN+SiLU with the other bands' current sums, conv3x3 with fresh halos,
     twice.  The neighbour bands' halos and sums are computed once beforehand;
-    only the rank's own calls are timed (HIP events on the launch stream)."""
+    only the rank's own calls are timed, each op back to back and the whole
+    band step back to back."""
     from displaced_patch_diffusion_amd.vae_rows import RowShardedResnet
     v = synth.VAE_LEVELS[name]
     inp = synth.vae_inputs(v)
@@ -341,34 +344,30 @@ def vae_rows_timing(torch, ops, synth, name: str, steps: int):
     y = torch.empty_like(x0)
     z = [torch.empty_like(x0), torch.empty_like(x0)]
     own = torch.empty((B, v.G, 2), dtype=torch.float32, device="cuda")
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(7)]
+    def layer_ops(i, xin):
+        sums, top, bot = layer[i]
+        return [("sums", lambda: ops.dp_groupnorm_sums(xin.view(B, T, v.C), v.G, out=own, ws=ws)),
+                ("gn", lambda: ops.dp_groupnorm_stale_stats(xin.view(B, T, v.C), sums, r, v.H * v.W,
+                                                            wts[f"gamma{i}"], wts[f"beta{i}"], v.eps, True, v.G,
+                                                            y=y.view(B, T, v.C), ws=ws)),
+                ("conv", lambda: ops.dp_conv3x3_stale_halo(y, top, bot, wts[f"w{i}"], wts[f"b{i}"], y=z[i]))]
+
+    band_ops = layer_ops(0, x0) + layer_ops(1, z[0])
 
     def band_step():
-        xin = x0
-        ev[0].record()
-        for i in range(2):
-            sums, top, bot = layer[i]
-            ops.dp_groupnorm_sums(xin.view(B, T, v.C), v.G, out=own, ws=ws)
-            ev[3 * i + 1].record()
-            ops.dp_groupnorm_stale_stats(xin.view(B, T, v.C), sums, r, v.H * v.W, wts[f"gamma{i}"],
-                                         wts[f"beta{i}"], v.eps, True, v.G, y=y.view(B, T, v.C), ws=ws)
-            ev[3 * i + 2].record()
-            ops.dp_conv3x3_stale_halo(y, top, bot, wts[f"w{i}"], wts[f"b{i}"], y=z[i])
-            ev[3 * i + 3].record()
-            xin = z[i]
+        for _, fn in band_ops:
+            fn()
 
     for _ in range(3):
         band_step()
     torch.cuda.synchronize()
+    # per op: its launches back to back (each op is idempotent on its inputs),
+    # averaged over the two layers; the whole band step back to back as well
     acc = {"sums": [], "gn": [], "conv": []}
-    for _ in range(steps):
-        band_step()
-        torch.cuda.synchronize()
-        for i in range(2):
-            acc["sums"].append(ev[3 * i].elapsed_time(ev[3 * i + 1]) * 1e3)
-            acc["gn"].append(ev[3 * i + 1].elapsed_time(ev[3 * i + 2]) * 1e3)
-            acc["conv"].append(ev[3 * i + 2].elapsed_time(ev[3 * i + 3]) * 1e3)
-    med = {k: float(np.median(a)) for k, a in acc.items()}
+    for name, fn in band_ops:
+        acc[name].append(back_to_back_us(torch, fn, steps))
+    med = {k: float(np.mean(a)) for k, a in acc.items()}
+    resnet = back_to_back_us(torch, band_step, steps)
     fl, gb = v.conv_flops(), v.gn_bytes()
     return {"workload": f"{v.name}: {v.note}; band {h}x{v.W}x{v.C}, batch {B}, rank {r} of {v.N}",
             "conv_us": round(med["conv"], 2), "conv_TFLOPs": round(fl / med["conv"] / 1e6, 1),
@@ -376,7 +375,7 @@ def vae_rows_timing(torch, ops, synth, name: str, steps: int):
             "groupnorm_sums_us": round(med["sums"], 2), "groupnorm_apply_us": round(med["gn"], 2),
             "groupnorm_GBps": round(gb / (med["sums"] + med["gn"]) / 1e3, 1),
             "groupnorm_frac": round(gb / (med["sums"] + med["gn"]) / 1e3 / PEAK_HBM_GBPS, 4),
-            "resnet_us": round(2 * (med["sums"] + med["gn"] + med["conv"]), 2)}
+            "resnet_us": round(resnet, 2)}
 
 
 # -------------------------------------------------------------- CPU baseline
