@@ -370,17 +370,33 @@ __global__ void __launch_bounds__(kThreads) gn_apply(GnArgs a) {
   if (!active) return;
   float ca[VEC], cb[VEC];
   channel_coeffs<VEC>(gstat, vi, a.C / G, gm, bt, ca, cb);
+  if (npass <= kUnroll) {  // one group of passes: its loads went out before the fold
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int t = t_begin + tl + u * tpp;
+      if (u < npass && t < t_end) normalize_store<BF16>(a, b, t, vi, first[u], ca, cb);
+    }
+    return;
+  }
+  // double-buffered: the loads of the next kUnroll passes go out before this
+  // group's normalise-and-store, so reads and writes stay in flight together
+  u32x4 cur[kUnroll];
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u) cur[u] = first[u];
   for (int k0 = 0; k0 < npass; k0 += kUnroll) {
-    u32x4 raw[kUnroll];
+    u32x4 nxt[kUnroll];
+    const bool more = k0 + kUnroll < npass;
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u)
-      raw[u] = k0 == 0 ? first[u]
-                       : load_or_zero<BF16>(a, b, t_begin + tl + (k0 + u) * tpp, t_end, vi, k0 + u < npass);
+      nxt[u] = load_or_zero<BF16>(a, b, t_begin + tl + (k0 + kUnroll + u) * tpp, t_end, vi,
+                                  more && k0 + kUnroll + u < npass);
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const int t = t_begin + tl + (k0 + u) * tpp;
-      if (k0 + u < npass && t < t_end) normalize_store<BF16>(a, b, t, vi, raw[u], ca, cb);
+      if (k0 + u < npass && t < t_end) normalize_store<BF16>(a, b, t, vi, cur[u], ca, cb);
     }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) cur[u] = nxt[u];
   }
 }
 
