@@ -246,6 +246,27 @@ def test_attention_balanced_schedule(B, H, Tq, Tkv):
         assert_close(host(out), ref, "bf16", f"attention, {sched} schedule")
 
 
+def test_attention_schedules_on_seeded_shapes():
+    """Both work schedules on 20 seeded random shapes (batch 1-3, 1-6 heads,
+    1-1500 queries, 1-6000 keys, plain and peaked queries): sampled rows of
+    every case against the oracle."""
+    rng = np.random.default_rng(1234)
+    for case in range(20):
+        B, H = int(rng.integers(1, 4)), int(rng.integers(1, 7))
+        Tq, Tkv = int(rng.integers(1, 1501)), int(rng.integers(1, 6001))
+        qs = float(rng.choice([1.0, 3.0]))
+        say("attn seeded shape", case, B, H, Tq, Tkv, qs)
+        q = R(10 + case, "ats.q", (B, Tq, H * 64), "bf16", qs)
+        k = R(10 + case, "ats.k", (B, Tkv, H * 64), "bf16")
+        v = R(10 + case, "ats.v", (B, Tkv, H * 64), "bf16")
+        rows = sample_rows(Tq, 6, case)
+        ref = oracle.attention(q[:, rows], k, v, H)
+        for sched in ("split", "balanced"):
+            with attn_schedule(sched):
+                out = host(ops.dp_attn_stale_kv(dev(q, "bf16"), dev(k, "bf16"), dev(v, "bf16"), H))
+            assert_close(out[:, rows], ref, "bf16", f"attention case {case}, {sched}")
+
+
 def test_attention_whole_rounds_then_split():
     """The split schedule with its full rounds run whole and only the last
     round's units split into key chunks (picked for 1000 query blocks on 768
