@@ -50,37 +50,48 @@ def log(*a):
 
 # ----------------------------------------------------------------- GPU state
 class Share:
-    """Device tensors of one rank's share plus its stale state."""
+    """Device tensors of one rank's share plus its stale state.
+
+    By default the stale state is the previous step's full-image result plus
+    N(0, 0.05^2) noise, computed here on the GPU.  `stale` instead hands it in
+    as host arrays (the parity tests draw it from the seeded generator): keys
+    k_buf, v_buf [B, T_kv, C]; halo_top{i}, halo_bot{i} [B, W, C] or None for
+    conv i; sums{i} [N, B, G, 2] float32 for GroupNorm i.  The ops and their
+    launch configuration are the same either way."""
 
     fused_qkv = True
     gn_sums_in_conv = False
 
-    def __init__(self, w, torch, ops, synth):
+    def __init__(self, w, torch, ops, synth, stale=None):
         self.w, self.torch, self.ops = w, torch, ops
         self.dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
         dev = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).cuda().to(self.dt)
         f32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).cuda()
+        opt = lambda a, fn: None if a is None else fn(a)
         noise = lambda name, shape: f32(synth.stale_noise(w, name, shape))
         B = w.B
         # ---------------- attention level
-        a = synth.attention_block_inputs(w)
+        a = synth.attention_block_inputs(w, with_noise=stale is None)
         H, Wd, C = w.attn_H, w.attn_W, w.attn_C
         T = H * Wd
         x_full = dev(a["x_full"]).view(B, T, C)
         self.wq, self.wk, self.wv, self.wo = (dev(a[k]) for k in ("wq", "wk", "wv", "wo"))
-        k_full = torch.empty((B, T, C), dtype=self.dt, device="cuda")
-        v_full = torch.empty_like(k_full)
-        for p in range(w.N):
-            a0, a1 = w.attn_rows(p)
-            xp = x_full[:, a0 * Wd:a1 * Wd].contiguous()
-            k_full[:, a0 * Wd:a1 * Wd] = ops.dp_linear(xp, self.wk)
-            v_full[:, a0 * Wd:a1 * Wd] = ops.dp_linear(xp, self.wv)
-        # stale buffers: the previous step's full-image K/V plus noise
-        self.k_buf = (k_full.float() + f32(a["k_noise"])).to(self.dt)
-        self.v_buf = (v_full.float() + f32(a["v_noise"])).to(self.dt)
         r0, r1 = w.attn_rows()
         self.t0 = r0 * Wd
         self.x_loc = x_full[:, r0 * Wd:r1 * Wd].contiguous()
+        if stale is None:
+            k_full = torch.empty((B, T, C), dtype=self.dt, device="cuda")
+            v_full = torch.empty_like(k_full)
+            for p in range(w.N):
+                a0, a1 = w.attn_rows(p)
+                xp = x_full[:, a0 * Wd:a1 * Wd].contiguous()
+                k_full[:, a0 * Wd:a1 * Wd] = ops.dp_linear(xp, self.wk)
+                v_full[:, a0 * Wd:a1 * Wd] = ops.dp_linear(xp, self.wv)
+            # stale buffers: the previous step's full-image K/V plus noise
+            self.k_buf = (k_full.float() + f32(a["k_noise"])).to(self.dt)
+            self.v_buf = (v_full.float() + f32(a["v_noise"])).to(self.dt)
+        else:
+            self.k_buf, self.v_buf = dev(stale["k_buf"]), dev(stale["v_buf"])
         Tq = w.Tq
         mk = lambda *s: torch.empty(*s, dtype=self.dt, device="cuda")
         self.q, self.kf, self.vf = mk(B, Tq, C), mk(B, Tq, C), mk(B, Tq, C)
@@ -93,7 +104,6 @@ class Share:
         G = w.G
         self.G = G
         hc, Wc, Cc, Hc = w.conv_h, w.conv_W, w.conv_C, w.conv_H
-        c0, c1 = w.conv_rows()
         self.hc, Tc = hc, hc * Wc
         self.convs, self.gns = [], []
         n_conv = 2 if w.two_level else 1
@@ -102,10 +112,36 @@ class Share:
             self.convs.append({"w": dev(cv["w"]), "b": f32(cv["bias"]), "cv": cv})
             gn = synth.groupnorm_inputs(w, i)
             self.gns.append({"gamma": f32(gn["gamma"]), "beta": f32(gn["beta"])})
-        # The previous step with stale == fresh, rebuilt rank by rank with the
-        # same launch shapes as the timed step; stale state = that + noise.
         rows_c = [w.conv_rows(p) for p in range(w.N)]
         band = lambda full, p: full[:, rows_c[p][0] * Wc:rows_c[p][1] * Wc]
+        self.conv_in_loc = None
+        if w.two_level:
+            z = dev(synth.conv_level_input(w)).view(B, Hc * Wc, Cc)
+            self.conv_in_loc = band(z, w.rank).contiguous()
+        if stale is not None:
+            for i in range(n_conv):
+                self.convs[i]["ht"] = opt(stale[f"halo_top{i}"], dev)
+                self.convs[i]["hb"] = opt(stale[f"halo_bot{i}"], dev)
+                self.gns[i]["stale"] = f32(stale[f"sums{i}"])
+        else:
+            self._previous_step(w, synth, x_full, k_full, v_full, band, rows_c, f32, noise)
+        self.gn_ws = torch.zeros(ops.dp_groupnorm_stale_stats_workspace(B, Tc, Cc, G),
+                                 dtype=torch.uint8, device="cuda")
+        self.zc = [mk(B, Tc, Cc) for _ in range(2)]
+        self.gc = [mk(B, Tc, Cc) for _ in range(2)]
+        self.fresh = [torch.empty((B, G, 2), dtype=torch.float32, device="cuda") for _ in range(2)]
+        self.conv_ws = torch.zeros(ops.dp_conv3x3_gn_sums_workspace(B, hc, Wc, Cc), dtype=torch.uint8,
+                                   device="cuda")
+        torch.cuda.synchronize()
+
+    def _previous_step(self, w, synth, x_full, k_full, v_full, band, rows_c, f32, noise):
+        """The previous step with stale == fresh, rebuilt rank by rank with the
+        same launch shapes as the timed step; stale state = that + noise."""
+        torch, ops = self.torch, self.ops
+        B, G = w.B, w.G
+        Wd = w.attn_W
+        hc, Wc, Cc, Hc = w.conv_h, w.conv_W, w.conv_C, w.conv_H
+        Tc = hc * Wc
 
         def halos(full_img, p, noise_t=None, noise_b=None):
             r0, r1 = rows_c[p]
@@ -119,8 +155,7 @@ class Share:
         def sums_of(full):
             out = torch.zeros((w.N, B, G, 2), dtype=torch.float32, device="cuda")
             for p in range(w.N):
-                ops.dp_groupnorm_stale_stats(band(full, p).contiguous(), None, 0, Tc, None, None,
-                                             w.eps, False, G, fresh_sums_out=out[p])
+                ops.dp_groupnorm_sums(band(full, p).contiguous(), G, out=out[p])
             return out
 
         def full_gn(full, i, silu):
@@ -138,9 +173,10 @@ class Share:
             out = torch.empty((B, Hc * Wc, Cc), dtype=self.dt, device="cuda")
             for p in range(w.N):
                 ht, hb = halos(img, p)
-                z = ops.dp_conv3x3_stale_halo(band(full, p).contiguous().view(B, hc, Wc, Cc), ht, hb,
-                                              self.convs[i]["w"], self.convs[i]["b"])
-                band(out, p).copy_(z.view(B, Tc, Cc))
+                z = ops.dp_conv3x3_stale_halo(band(full, p).contiguous().view(B, rows_c[p][1] - rows_c[p][0],
+                                                                               Wc, Cc),
+                                              ht, hb, self.convs[i]["w"], self.convs[i]["b"])
+                band(out, p).copy_(z.view(B, -1, Cc))
             return out
 
         def stale_sums(full, i):
@@ -152,15 +188,17 @@ class Share:
                          f32(cv["halo_bot_noise"]))
 
         if w.two_level:
-            z = dev(synth.conv_level_input(w)).view(B, Hc * Wc, Cc)
-            self.conv_in_loc = band(z, w.rank).contiguous()
+            z = torch.empty((B, Hc * Wc, Cc), dtype=self.dt, device="cuda")
+            z.copy_(torch.from_numpy(np.ascontiguousarray(synth.conv_level_input(w), np.float32))
+                    .cuda().to(self.dt).view(B, Hc * Wc, Cc))
             for i in range(2):
                 self.gns[i]["stale"] = stale_sums(z, i)
                 g_full = full_gn(z, i, True)
                 self.convs[i]["ht"], self.convs[i]["hb"] = stale_halos(g_full, i)
                 z = full_conv(g_full, i)
         else:
-            y_full = torch.empty((B, T, C), dtype=self.dt, device="cuda")
+            T = w.T_kv
+            y_full = torch.empty((B, T, w.attn_C), dtype=self.dt, device="cuda")
             for p in range(w.N):
                 a0, a1 = w.attn_rows(p)
                 xp = x_full[:, a0 * Wd:a1 * Wd].contiguous()
@@ -169,16 +207,6 @@ class Share:
             self.convs[0]["ht"], self.convs[0]["hb"] = stale_halos(y_full, 0)
             z = full_conv(y_full, 0)
             self.gns[0]["stale"] = stale_sums(z, 0)
-        self.gn_ws = torch.empty(ops.dp_groupnorm_stale_stats_workspace(B, Tc, Cc, G),
-                                 dtype=torch.uint8, device="cuda")
-        self.zc = [mk(B, Tc, Cc) for _ in range(2)]
-        self.gc = [mk(B, Tc, Cc) for _ in range(2)]
-        self.fresh = [torch.empty((B, G, 2), dtype=torch.float32, device="cuda") for _ in range(2)]
-        self.conv_ws = torch.empty(ops.dp_conv3x3_gn_sums_workspace(B, hc, Wc, Cc), dtype=torch.uint8,
-                                   device="cuda")
-        if not w.two_level:
-            self.conv_in_loc = None
-        torch.cuda.synchronize()
 
     # the ops of one step, in order, as (name, enqueue function)
     def op_list(self):
@@ -251,6 +279,24 @@ class Share:
 
     def prepare(self):
         self.ops_ = self.op_list()
+
+
+DEFAULT_QKV = "fused"
+DEFAULT_GN_SUMS = "separate"
+
+
+def make_share(w, qkv: str = DEFAULT_QKV, gn_sums: str = DEFAULT_GN_SUMS):
+    """The share of workload `w` with its stale state on the GPU, its op list
+    prepared exactly as the timed steps run it."""
+    import torch
+
+    from displaced_patch_diffusion_amd import ops, synth
+
+    share = Share(w, torch, ops, synth)
+    share.fused_qkv = qkv == "fused"
+    share.gn_sums_in_conv = gn_sums == "conv"
+    share.prepare()
+    return share
 
 
 def back_to_back_us(torch, fn, reps: int) -> float:
@@ -481,12 +527,12 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle's attention sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--gn-sums", choices=("conv", "separate"), default="separate",
+    ap.add_argument("--gn-sums", choices=("conv", "separate"), default=DEFAULT_GN_SUMS,
                     help="conv: the conv epilogue forms the GroupNorm's local sums and the GroupNorm is one "
                          "pass; separate: the GroupNorm forms them in a read pass of its own")
     ap.add_argument("--no-otil", action="store_true", help="skip the OTIL selective-transmit timing")
     ap.add_argument("--no-vae", action="store_true", help="skip the row-sharded VAE decoder timing")
-    ap.add_argument("--qkv", choices=("fused", "separate"), default="fused",
+    ap.add_argument("--qkv", choices=("fused", "separate"), default=DEFAULT_QKV,
                     help="fused: one launch projects Q/K/V and writes K/V into the buffers; "
                          "separate: three projections then the K/V splice")
     args = ap.parse_args()
@@ -506,10 +552,7 @@ def main():
     w = synth.WORKLOADS[args.workload]
     torch.cuda.set_device(0)
     log(f"bench: workload {w.name}: building inputs")
-    share = Share(w, torch, ops, synth)
-    share.fused_qkv = args.qkv == "fused"
-    share.gn_sums_in_conv = args.gn_sums == "conv"
-    share.prepare()
+    share = make_share(w, args.qkv, args.gn_sums)
 
     names = []
 

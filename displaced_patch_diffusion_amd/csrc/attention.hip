@@ -626,19 +626,36 @@ int device_cus() {
   return cached_cus;
 }
 
-// Resident attention blocks per CU (registers and LDS), asked of the runtime.
+// Resident attention blocks per CU (registers and LDS), asked of the runtime
+// once per device and thread.
 template <bool SK>
 int blocks_per_cu() {
-  static thread_local int cached = 0;
-  if (cached == 0) {
-    int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_bf16_d64<SK>, 256, 0) != hipSuccess || n <= 0) {
-      (void)hipGetLastError();
-      n = 2;
-    }
-    cached = n;
+  constexpr int kMaxDev = 64;
+  static thread_local int cached[kMaxDev] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    dev = -1;
   }
-  return cached;
+  if (dev >= 0 && dev < kMaxDev && cached[dev] > 0) return cached[dev];
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_bf16_d64<SK>, 256, 0) != hipSuccess || n <= 0) {
+    (void)hipGetLastError();
+    n = 2;
+  }
+  if (dev >= 0 && dev < kMaxDev) cached[dev] = n;
+  return n;
+}
+
+// Schedule override from DP_ATTN_SCHEDULE (tests and tuning): 0 none,
+// 1 split, 2 balanced.
+enum { kSchedAuto = 0, kSchedSplit = 1, kSchedBalanced = 2 };
+int schedule_override() {
+  const char* env = getenv("DP_ATTN_SCHEDULE");
+  if (!env) return kSchedAuto;
+  if (strcmp(env, "split") == 0) return kSchedSplit;
+  if (strcmp(env, "balanced") == 0) return kSchedBalanced;
+  return kSchedAuto;
 }
 
 // Picks the schedule.  Split schedule: the number of key chunks; each block
@@ -647,7 +664,7 @@ int blocks_per_cu() {
 // per XCD) x (tiles per unit), plus the cost of the extra partial-output
 // traffic when the keys are split.  The balanced schedule is priced the same
 // way: tiles per resident block plus its partial traffic.
-AttnPlan plan_attention(int64_t B, int64_t H, int64_t Tq, int64_t Tkv) {
+AttnPlan plan_attention(int64_t B, int64_t H, int64_t Tq, int64_t Tkv, int sched) {
   AttnPlan p{};
   p.n_qblk = static_cast<int>((Tq + kBMq - 1) / kBMq);
   p.n_tiles = static_cast<int>((Tkv + kBNk - 1) / kBNk);
@@ -690,9 +707,8 @@ AttnPlan plan_attention(int64_t B, int64_t H, int64_t Tq, int64_t Tkv) {
   // staggered offsets instead of in step with the other query blocks of their
   // (batch, head), so their L2 reuse is lower: taken only where the K/V
   // buffers fit well inside the last-level cache (half of its 256 MB) and the
-  // estimate beats the split schedule by 3%.  DP_ATTN_SCHEDULE=split or
-  // =balanced in the environment overrides the choice (for tests and tuning;
-  // the workspace query and the call must see the same setting).
+  // estimate beats the split schedule by 3%.  `sched` forces either
+  // schedule (DP_ATTN_SCHEDULE=split or =balanced, for tests and tuning).
   {
     const int sk_slots = std::max(1, device_cus() / kXcds) * blocks_per_cu<true>() * kXcds;
     const long long work = static_cast<long long>(base_units) * p.n_tiles;
@@ -700,9 +716,8 @@ AttnPlan plan_attention(int64_t B, int64_t H, int64_t Tq, int64_t Tkv) {
     const double sk_cost = per_slot + 2.0 * tile_cost +
                            (2.0 * sk_slots * kBMq * kD * 8.0 + 2.0 * B * Tq * H * kD) / bytes_per_tile_cost;
     const double kv_bytes = 2.0 * B * Tkv * H * kD * 2;
-    const char* env = getenv("DP_ATTN_SCHEDULE");
-    const bool force_sk = env && strcmp(env, "balanced") == 0;
-    const bool force_split = env && strcmp(env, "split") == 0;
+    const bool force_sk = sched == kSchedBalanced;
+    const bool force_split = sched == kSchedSplit;
     if (!force_split && (force_sk || (sk_cost < best * 0.97 && kv_bytes <= 128.0e6))) {
       p.sk = 1;
       p.work = work;
@@ -793,7 +808,10 @@ attn_f32(const float* __restrict__ q, const float* __restrict__ k, const float* 
 DP_API size_t dp_attn_stale_kv_workspace(int64_t B, int64_t H, int64_t Tq, int64_t T_kv, int64_t d,
                                          dp_dtype dt) {
   if (dt != DP_BF16 || d != kD || B <= 0 || H <= 0 || Tq <= 0 || T_kv <= 0) return 0;
-  return plan_attention(B, H, Tq, T_kv).ws_bytes;
+  // Enough for either schedule, so the size does not depend on which one a
+  // later call picks (or is forced to).
+  return std::max(plan_attention(B, H, Tq, T_kv, kSchedSplit).ws_bytes,
+                  plan_attention(B, H, Tq, T_kv, kSchedBalanced).ws_bytes);
 }
 
 DP_API dp_status dp_attn_stale_kv(const void* q, const void* k_buf, const void* v_buf, void* out,
@@ -819,7 +837,7 @@ DP_API dp_status dp_attn_stale_kv(const void* q, const void* k_buf, const void* 
   if (dt == DP_BF16) {
     if (T_kv * H * d > 0x7FFFFFFF || Tq * H * d > 0x7FFFFFFF)
       return fail(DP_ERR_UNSUPPORTED, "dp_attn_stale_kv: one batch item exceeds 2^31 elements");
-    const AttnPlan p = plan_attention(B, H, Tq, T_kv);
+    const AttnPlan p = plan_attention(B, H, Tq, T_kv, schedule_override());
     if (p.ws_bytes > 0 && (!ws || ws_bytes < p.ws_bytes))
       return fail(DP_ERR_INVALID_ARG, "dp_attn_stale_kv: workspace %zu < %zu bytes", ws_bytes, p.ws_bytes);
     AttnArgs args;

@@ -35,11 +35,7 @@ import time
 import torch
 
 from . import ops
-
-
-def partition(H: int, N: int) -> list[tuple[int, int]]:
-    """Row bands [floor(r H / N), floor((r+1) H / N))."""
-    return [((r * H) // N, ((r + 1) * H) // N) for r in range(N)]
+from .partition import row_bands
 
 
 class DisplacedSchedule:
@@ -49,7 +45,7 @@ class DisplacedSchedule:
         self.w = weights
         dt = weights["wq"].dtype
         dev = weights["wq"].device
-        self.bands = partition(H, N)
+        self.bands = row_bands(H, N)
         T = H * W
 
         def buf(*shape, dtype=dt):

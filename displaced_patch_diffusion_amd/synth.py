@@ -23,6 +23,8 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
+from .partition import row_band
+
 SEED_WEIGHTS = 0
 SEED_ACTIVATIONS = 1
 SEED_STALE = 2
@@ -107,8 +109,7 @@ class Workload:
         return self.attn_H * self.attn_W
 
     def rows(self, H: int, r: int | None = None) -> tuple[int, int]:
-        r = self.rank if r is None else r
-        return (r * H) // self.N, ((r + 1) * H) // self.N
+        return row_band(H, self.N, self.rank if r is None else r)
 
     def attn_rows(self, r: int | None = None) -> tuple[int, int]:
         return self.rows(self.attn_H, r)
@@ -206,10 +207,11 @@ def normal(seed: int, name: str, shape, std: float = 1.0, mean: float = 0.0) -> 
     return a
 
 
-def attention_block_inputs(w: Workload) -> dict:
-    """Full-image activations, the four projection weights and the stale-step
-    noise for the attention level.  Stale K/V = (projection of the full image)
-    + noise; the projection is left to the caller."""
+def attention_block_inputs(w: Workload, with_noise: bool = True) -> dict:
+    """Full-image activations, the four projection weights and (unless
+    with_noise is False) the stale-step noise for the attention level.  Stale
+    K/V = (projection of the full image) + noise; the projection is left to
+    the caller."""
     B, H, W, C, dt = w.B, w.attn_H, w.attn_W, w.attn_C, w.dtype
     s = 1.0 / np.sqrt(C)
     out = {
@@ -218,9 +220,39 @@ def attention_block_inputs(w: Workload) -> dict:
         "wk": as_storage(normal(SEED_WEIGHTS, "attn.wk", (C, C), s), dt),
         "wv": as_storage(normal(SEED_WEIGHTS, "attn.wv", (C, C), s), dt),
         "wo": as_storage(normal(SEED_WEIGHTS, "attn.wo", (C, C), s), dt),
-        "k_noise": normal(SEED_STALE, "attn.k_noise", (B, H * W, C), w.noise),
-        "v_noise": normal(SEED_STALE, "attn.v_noise", (B, H * W, C), w.noise),
     }
+    if with_noise:
+        out["k_noise"] = normal(SEED_STALE, "attn.k_noise", (B, H * W, C), w.noise)
+        out["v_noise"] = normal(SEED_STALE, "attn.v_noise", (B, H * W, C), w.noise)
+    return out
+
+
+def drawn_stale_state(w: Workload) -> dict:
+    """A stale state drawn directly from the seeded streams, for parity runs
+    whose expected values must not depend on a previous step computed on the
+    device: remote K/V buffers ~ N(0,1) (the distribution of x W^T with
+    x ~ N(0,1), W ~ N(0, 1/C)), halo rows ~ N(0,1) where the band has a
+    neighbour, and the remote activations whose group sums stand for the other
+    patches' stale sums (the sums themselves are arithmetic and are left to the
+    caller).  Keys: k_buf, v_buf [B, T_kv, C]; halo_top{i}, halo_bot{i}
+    [B, W, C] or None; remote{i} [N, B, T_band, C] for conv/GroupNorm layer i
+    (the rank's own entry is drawn too and must never be read)."""
+    B, C, dt = w.B, w.attn_C, w.dtype
+    out = {
+        "k_buf": as_storage(normal(SEED_STALE, "drawn.k_buf", (B, w.T_kv, C)), dt),
+        "v_buf": as_storage(normal(SEED_STALE, "drawn.v_buf", (B, w.T_kv, C)), dt),
+    }
+    r0, r1 = w.conv_rows()
+    Cc, Wc = w.conv_C, w.conv_W
+    for i in range(2 if w.two_level else 1):
+        out[f"halo_top{i}"] = (as_storage(normal(SEED_STALE, f"drawn.halo_top{i}", (B, Wc, Cc)), dt)
+                               if r0 > 0 else None)
+        out[f"halo_bot{i}"] = (as_storage(normal(SEED_STALE, f"drawn.halo_bot{i}", (B, Wc, Cc)), dt)
+                               if r1 < w.conv_H else None)
+        out[f"remote{i}"] = [
+            as_storage(normal(SEED_STALE, f"drawn.remote{i}.{p}", (B, (w.conv_rows(p)[1] - w.conv_rows(p)[0]) * Wc, Cc),
+                              1.1 + 0.1 * p, 0.05 * p), dt)
+            for p in range(w.N)]
     return out
 
 
@@ -317,8 +349,7 @@ class VaeLevel:
     note: str = field(default="", compare=False)
 
     def rows(self, r: int | None = None) -> tuple[int, int]:
-        r = self.rank if r is None else r
-        return (r * self.H) // self.N, ((r + 1) * self.H) // self.N
+        return row_band(self.H, self.N, self.rank if r is None else r)
 
     @property
     def h(self) -> int:

@@ -15,6 +15,7 @@ from __future__ import annotations
 import torch
 
 from . import ops
+from .partition import row_bands
 
 
 class RowShardedResnet:
@@ -23,7 +24,7 @@ class RowShardedResnet:
     def __init__(self, H: int, W: int, C: int, N: int, weights: dict, G: int = 32, eps: float = 1e-5):
         self.H, self.W, self.C, self.N, self.G, self.eps = H, W, C, N, G, eps
         self.wt = weights
-        self.bands = [((r * H) // N, ((r + 1) * H) // N) for r in range(N)]
+        self.bands = row_bands(H, N)
 
     def _gn(self, xs: list, i: int) -> list:
         """GroupNorm+SiLU of every band with whole-image statistics."""

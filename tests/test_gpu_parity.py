@@ -165,15 +165,17 @@ def test_groupnorm_single_patch_null_stale():
 
 
 # ------------------------------------------------------------------ attention
-@pytest.mark.parametrize("dt,B,H,d,Tq,Tkv", [
-    ("bf16", 2, 2, 64, 200, 333), ("bf16", 1, 3, 64, 128, 64), ("bf16", 2, 1, 64, 5, 1),
-    ("bf16", 1, 2, 64, 257, 1000), ("f32", 2, 2, 32, 512, 1024), ("f32", 1, 3, 64, 100, 77),
-    ("f32", 1, 1, 32, 3, 1),
-])
-@pytest.mark.parametrize("schedule", [None, "balanced"])
+_ATTN_BF16 = [("bf16", 2, 2, 64, 200, 333), ("bf16", 1, 3, 64, 128, 64), ("bf16", 2, 1, 64, 5, 1),
+              ("bf16", 1, 2, 64, 257, 1000)]
+_ATTN_F32 = [("f32", 2, 2, 32, 512, 1024), ("f32", 1, 3, 64, 100, 77), ("f32", 1, 1, 32, 3, 1)]
+
+
+# bf16 cases under the planner's pick and each forced schedule; the f32 path
+# has one schedule
+@pytest.mark.parametrize("dt,B,H,d,Tq,Tkv,schedule",
+                         [c + (s,) for c in _ATTN_BF16 for s in (None, "split", "balanced")] +
+                         [c + (None,) for c in _ATTN_F32])
 def test_attention(dt, B, H, d, Tq, Tkv, schedule):
-    if dt == "f32" and schedule is not None:
-        pytest.skip("the f32 path has one schedule")
     say("attn", dt, B, H, d, Tq, Tkv, schedule)
     q = R(1, "at.q", (B, Tq, H * d), dt)
     k = R(1, "at.k", (B, Tkv, H * d), dt)
@@ -571,6 +573,13 @@ def test_stale_equals_fresh_ranks_concat_on_gpu():
     # the one for a share (1024 queries), so the summation order differs: the
     # property holds to the bf16 tolerance, not bit for bit.
     assert_close(host(cat), host(ref), "bf16", "stale==fresh concatenation")
+    # and both equal the oracle's unsplit attention of the full image (float64
+    # projections from the same inputs) on one query row per 128-query block
+    xf = a["x_full"].reshape(B, Hh * Wd, C)
+    rows = np.arange(17, Hh * Wd, 128)
+    ref_o = oracle.attention(oracle.linear(xf[:, rows], a["wq"]), oracle.linear(xf, a["wk"]),
+                             oracle.linear(xf, a["wv"]), w.heads)
+    assert_close(host(cat)[:, rows], ref_o, "bf16", "stale==fresh concatenation vs oracle")
 
 
 # ------------------------------------------- fused Q/K/V projection (NEXT-2)

@@ -151,5 +151,10 @@ def test_multi_rank_reconstruction_rules():
                     else:
                         assert np.array_equal(got, otil.block_view(band_old, j, bh, bw))
             assert np.array_equal(copies[r][:, r * h:(r + 1) * h], latent[:, r * h:(r + 1) * h])
-    gathered = np.concatenate([latent[:, p * h:(p + 1) * h] for p in range(N)], axis=1)
+    # The pre-decode gather takes each rank's own band from that rank's copy:
+    # it is exact, although every rank's copy is stale somewhere remote.
+    gathered = np.concatenate([copies[p][:, p * h:(p + 1) * h] for p in range(N)], axis=1)
     assert np.array_equal(gathered, latent)
+    for r in range(N):
+        remote = np.r_[0:r * h, (r + 1) * h:H]
+        assert not np.array_equal(copies[r][:, remote], latent[:, remote])
