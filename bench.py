@@ -386,7 +386,7 @@ def vae_rows_timing(torch, ops, synth, name: str, steps: int):
     x0 = x[:, net.bands[r][0]:net.bands[r][1]].contiguous()
     h = x0.shape[1]
     T = h * v.W
-    ws = torch.empty(ops.dp_groupnorm_stale_stats_workspace(B, T, v.C, v.G), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(ops.dp_groupnorm_stale_stats_workspace(B, T, v.C, v.G), dtype=torch.uint8, device="cuda")
     y = torch.empty_like(x0)
     z = [torch.empty_like(x0), torch.empty_like(x0)]
     own = torch.empty((B, v.G, 2), dtype=torch.float32, device="cuda")

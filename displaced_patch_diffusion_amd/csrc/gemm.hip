@@ -20,6 +20,7 @@
 // accumulator lane holds 4 consecutive output channels of one output row and
 // the epilogue writes 8-byte runs.
 // f32 path: a plain LDS-tiled FMA kernel (correctness path for fp32 shares).
+#include <algorithm>
 #include <cmath>
 
 #include "dp_internal.h"
@@ -69,9 +70,97 @@ struct GemmArgs {
   const float* bias;   // [N] or null
   int M, N, K;
   int tiles_m, tiles_n, units, units_per_xcd;
-  float2* gpart;       // GroupNorm partials [tiles_m * WGM][2][N] (conv with sums only)
-  int gT;              // output tokens per batch item (conv with sums only)
+  // conv with GroupNorm sums only:
+  float2* gpart;       // per (tile row, batch segment, tile column, group slot) partials
+  unsigned* counters;  // ticket counters per batch item, kCounterStride apart
+  float* gsums;        // [B][G][2] output
+  int gT;              // output tokens per batch item
+  int G, Cg, slots, counter_stride;
+  int ticket;          // 1: the last tile of each batch item folds its sums; 0: a fold launch follows
 };
+
+constexpr int kTicketGroup = 16;    // tiles per first-level ticket counter
+constexpr int kCounterStride = 32;  // uints between counters (one 128-byte line each)
+// Ticket counters live in a fixed region at the start of the workspace, the
+// same for every shape, and nothing else is ever written there: a workspace
+// zero-filled once stays valid for any sequence of calls.
+constexpr int kCounterBytes = 32768;
+// The last tile folds its batch item's partials only up to this many bytes of
+// them (a one-block fold); larger folds run as their own launch.
+constexpr int kTicketFoldBytes = 65536;
+
+// Device-coherent 8-byte store and load (agent scope: they bypass the per-XCD
+// L2, so blocks on other XCDs see them within the same launch).
+__device__ __forceinline__ void store_coherent(float2* p, float2 v) {
+  __hip_atomic_store(reinterpret_cast<unsigned long long*>(p), __builtin_bit_cast(unsigned long long, v),
+                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float2 load_coherent(const float2* p) {
+  return __builtin_bit_cast(float2, __hip_atomic_load(reinterpret_cast<const unsigned long long*>(p),
+                                                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+}
+
+// Tile rows [lo, hi] holding the output rows of batch item b.
+__device__ __forceinline__ int2 batch_tile_rows(int b, int gT, int BM) {
+  return make_int2(static_cast<int>((static_cast<int64_t>(b) * gT) / BM),
+                   static_cast<int>(((static_cast<int64_t>(b) + 1) * gT - 1) / BM));
+}
+
+// Partial of group gi from the tile (tr, tc) for batch item b: the slot the
+// tile stored for that group.
+__device__ __forceinline__ const float2* gn_slot(const GemmArgs& g, int b, int gi, int tr, int tc, int BM, int BN) {
+  const int sgt = b - static_cast<int>((static_cast<int64_t>(tr) * BM) / g.gT);
+  return g.gpart + ((static_cast<int64_t>(tr) * 2 + sgt) * g.tiles_n + tc) * g.slots + gi - (tc * BN) / g.Cg;
+}
+
+// Sum over the partials of group gi for batch item b that lane q of `lanes`
+// owns: the (tile row, tile column) pairs e = q, q + lanes, ... in order,
+// eight loads in flight at a time.  COH selects device-coherent loads (inside
+// the launch that wrote them).
+template <bool COH>
+__device__ float2 fold_group_lane(const GemmArgs& g, int b, int gi, int q, int lanes, int BM, int BN) {
+  const int2 r = batch_tile_rows(b, g.gT, BM);
+  const int tn_lo = (gi * g.Cg) / BN, ntn = ((gi + 1) * g.Cg - 1) / BN - tn_lo + 1;
+  const int total = (r.y - r.x + 1) * ntn;
+  constexpr int U = 8;
+  float2 s = make_float2(0.f, 0.f);
+  for (int e0 = q; e0 < total; e0 += U * lanes) {
+    float2 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int e = min(e0 + u * lanes, total - 1);
+      const float2* p = gn_slot(g, b, gi, r.x + e / ntn, tn_lo + e % ntn, BM, BN);
+      v[u] = COH ? load_coherent(p) : *p;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (e0 + u * lanes < total) {
+        s.x += v[u].x;
+        s.y += v[u].y;
+      }
+    }
+  }
+  return s;
+}
+
+// Counts tile (tm, tn) in for batch item b; true for exactly one tile, the last
+// of the item's tiles to arrive (two-level: kTicketGroup tiles per first-level
+// counter).  Every counter is back at zero once all tiles have arrived.
+__device__ bool take_batch_ticket(const GemmArgs& g, int b, int tm, int tn, int BM) {
+  const int2 r = batch_tile_rows(b, g.gT, BM);
+  const int n_tiles = (r.y - r.x + 1) * g.tiles_n;
+  const int idx = (tm - r.x) * g.tiles_n + tn;
+  const int grp = idx / kTicketGroup;
+  const unsigned in_grp = static_cast<unsigned>(min(kTicketGroup, n_tiles - grp * kTicketGroup));
+  const unsigned n_grp = static_cast<unsigned>((n_tiles + kTicketGroup - 1) / kTicketGroup);
+  unsigned* base = g.counters + static_cast<int64_t>(b) * g.counter_stride;
+  unsigned* gc = base + (1 + grp) * kCounterStride;
+  if (__hip_atomic_fetch_add(gc, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != in_grp - 1) return false;
+  __hip_atomic_store(gc, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (__hip_atomic_fetch_add(base, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != n_grp - 1) return false;
+  __hip_atomic_store(base, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return true;
+}
 
 // LDS rows of 64 bytes (BK = 32) or 128 bytes (BK = 64): 16-byte chunk c of
 // row r lives in slot c ^ swz(r), chosen so the 16 rows one operand read
@@ -318,9 +407,22 @@ __global__ void __launch_bounds__(64 * NW, OCC) gemm_bf16(GemmArgs g) {
     }
   }
 
+  // Bias of the lane's 16 channels of column block i, loaded into registers
+  // once: read inside the store loop, the compiler reloads it (and waits for
+  // it) after every store, one memory round trip per row block.
+  auto bias_of = [&](int i, float (&bq)[4][4]) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        bq[q][e] = g.bias ? g.bias[min(n0 + wn * WN + 32 * i + 8 * q + 4 * gq + e, g.N - 1)] : 0.f;
+  };
+
   // Epilogue: lane holds rows n = 8*(e/4) + 4*gq + e%4 of column m = l32.
 #pragma unroll
-  for (int i = 0; i < NB; ++i)
+  for (int i = 0; i < NB; ++i) {
+    float bq[4][4];
+    bias_of(i, bq);
 #pragma unroll
     for (int j = 0; j < MB; ++j) {
       const int m = m0 + wm * WM + 32 * j + l32;
@@ -334,27 +436,33 @@ __global__ void __launch_bounds__(64 * NW, OCC) gemm_bf16(GemmArgs g) {
         const int n = nblk + 8 * q + 4 * gq;
         float v[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * q + e] + (g.bias ? g.bias[n + e] : 0.f);
+        for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * q + e] + bq[q][e];
         u32x2 packed = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
         *reinterpret_cast<u32x2*>(yrow + n) = packed;
       }
     }
+  }
 
   if constexpr (GNS) {
-    // GroupNorm partials of the stored (bf16-rounded) outputs: per channel,
-    // (sum y, sum y^2) over this wave's rows of the batch item of the tile's
-    // first row (segment 0) and of the next one (segment 1; a tile spans at
-    // most two since gT >= BM).  Rows are summed in-lane over the row blocks,
-    // then across the 32 lanes of each half-wave by a fixed butterfly, so the
-    // result does not depend on scheduling.
-    const int mw0 = m0 + wm * WM;
+    // GroupNorm sums of the stored (bf16-rounded) outputs.  Per channel, each
+    // wave sums its rows of the batch item of the tile's first row (segment
+    // 0) and of the next one (segment 1; a tile spans at most two since
+    // gT >= BM): in-lane over its row blocks, then across the 32 lanes of each
+    // half-wave by a fixed butterfly.  The block then sums, in LDS, its waves
+    // and the channels of each group its columns touch, in a fixed order, and
+    // stores one partial per (batch segment, group slot).  The last tile of a
+    // batch item to finish folds that item's partials into gsums.
+    float2* chan = reinterpret_cast<float2*>(lds);  // [2][WGM][BN]
     const int b0 = m0 / g.gT;
     const int nseg = (min(m0 + BM, g.M) - 1) / g.gT - b0 + 1;
-    float2* prow = g.gpart + (static_cast<int64_t>(tm) * WGM + wm) * 2 * g.N;
+    const int mw0 = m0 + wm * WM;
+    __syncthreads();  // every wave is past its last operand read of the ring
     for (int sg = 0; sg < nseg; ++sg) {
 #pragma unroll
       for (int i = 0; i < NB; ++i) {
         const int nblk = n0 + wn * WN + 32 * i;
+        float bq[4][4];
+        bias_of(i, bq);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {  // channels nblk + 8q + 4gq + (0..3)
           float s1[4] = {0.f, 0.f, 0.f, 0.f}, s2[4] = {0.f, 0.f, 0.f, 0.f};
@@ -364,9 +472,7 @@ __global__ void __launch_bounds__(64 * NW, OCC) gemm_bf16(GemmArgs g) {
             const bool on = m < g.M && m / g.gT - b0 == sg && nblk < g.N;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-              const int n = min(nblk + 8 * q + 4 * gq + e, g.N - 1);
-              const float v =
-                  static_cast<float>(static_cast<__bf16>(acc[i][j][4 * q + e] + (g.bias ? g.bias[n] : 0.f)));
+              const float v = static_cast<float>(static_cast<__bf16>(acc[i][j][4 * q + e] + bq[q][e]));
               s1[e] += on ? v : 0.f;
               s2[e] += on ? v * v : 0.f;
             }
@@ -378,49 +484,84 @@ __global__ void __launch_bounds__(64 * NW, OCC) gemm_bf16(GemmArgs g) {
               s1[e] += __shfl_xor(s1[e], off, 64);
               s2[e] += __shfl_xor(s2[e], off, 64);
             }
-          if (l32 == 0 && nblk < g.N) {
+          if (l32 == 0) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) prow[sg * g.N + nblk + 8 * q + 4 * gq + e] = make_float2(s1[e], s2[e]);
+            for (int e = 0; e < 4; ++e)
+              chan[(sg * WGM + wm) * BN + wn * WN + 32 * i + 8 * q + 4 * gq + e] = make_float2(s1[e], s2[e]);
           }
         }
+      }
+    }
+    __syncthreads();
+    const int n1 = min(n0 + BN, g.N);
+    const int g_lo = n0 / g.Cg, nslots = (n1 - 1) / g.Cg - g_lo + 1;
+    for (int t = tid; t < nseg * nslots; t += 64 * NW) {
+      const int sg = t / nslots, jj = t - sg * nslots, gi = g_lo + jj;
+      const int c0 = max(gi * g.Cg, n0), c1 = min((gi + 1) * g.Cg, n1);
+      float2 acc2 = make_float2(0.f, 0.f);
+      for (int c = c0; c < c1; ++c)
+#pragma unroll
+        for (int w = 0; w < WGM; ++w) {
+          const float2 v = chan[(sg * WGM + w) * BN + c - n0];
+          acc2.x += v.x;
+          acc2.y += v.y;
+        }
+      store_coherent(g.gpart + ((static_cast<int64_t>(tm) * 2 + sg) * g.tiles_n + tn) * g.slots + jj, acc2);
+    }
+    if (!g.ticket) return;
+    // the block's partials are complete at the coherence point before its tickets
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    __shared__ int fold_mask;
+    if (tid == 0) {
+      int mask = 0;
+      for (int sg = 0; sg < nseg; ++sg)
+        if (take_batch_ticket(g, b0 + sg, tm, tn, BM)) mask |= 1 << sg;
+      fold_mask = mask;
+    }
+    __syncthreads();
+    const int mask = fold_mask;
+    for (int sg = 0; sg < nseg; ++sg) {
+      if (!(mask & (1 << sg))) continue;
+      // fold batch item b: lane q of each group takes its share of the
+      // group's (tile row, tile column) partials; the lanes are added in order
+      const int b = b0 + sg;
+      const int lanes = g.G >= 64 * NW ? 1 : (64 * NW) / g.G;
+      float2* red = chan;  // [lanes][G], free again after the barrier above
+      __syncthreads();
+      for (int f = tid; f < lanes * g.G; f += 64 * NW)
+        red[f] = fold_group_lane<true>(g, b, f % g.G, f / g.G, lanes, BM, BN);
+      __syncthreads();
+      for (int gi = tid; gi < g.G; gi += 64 * NW) {
+        float2 sum = red[gi];
+        for (int q = 1; q < lanes; ++q) {
+          sum.x += red[q * g.G + gi].x;
+          sum.y += red[q * g.G + gi].y;
+        }
+        g.gsums[(static_cast<int64_t>(b) * g.G + gi) * 2] = sum.x;
+        g.gsums[(static_cast<int64_t>(b) * g.G + gi) * 2 + 1] = sum.y;
       }
     }
   }
 }
 
-// Folds the conv epilogue's GroupNorm partials into (sum, sum of squares) per
-// (batch item, group): one block per (group, batch item).  The partials of
-// the item's tiles (tiles in order, then wave row groups, then the group's
-// channels) are dealt to the threads round-robin, summed in order per thread,
-// then combined by a fixed tree: deterministic.
+// The fold as a launch of its own (one block per (group, batch item)), for
+// convs whose partials are too many for one block: 256 lanes, added in order.
 constexpr int kFoldThreads = 256;
-__global__ void __launch_bounds__(kFoldThreads)
-gn_conv_fold(const float2* __restrict__ gpart, float* __restrict__ out, int N, int G, int gT, int BM, int WGM) {
+template <int BM, int BN>
+__global__ void __launch_bounds__(kFoldThreads) gn_conv_fold(GemmArgs g) {
   __shared__ float2 red[kFoldThreads];
-  const int gi = blockIdx.x, b = blockIdx.y, Cg = N / G;
-  const int tm_lo = (b * gT) / BM, tm_hi = ((b + 1) * gT - 1) / BM;
-  const int total = (tm_hi - tm_lo + 1) * WGM * Cg;
-  float2 acc = make_float2(0.f, 0.f);
-  for (int e = threadIdx.x; e < total; e += kFoldThreads) {
-    const int c = e % Cg, r = e / Cg;
-    const int w = r % WGM, tm = tm_lo + r / WGM;
-    const int sg = b - (tm * BM) / gT;
-    const float2 p = gpart[(static_cast<int64_t>(tm) * WGM + w) * 2 * N + sg * N + gi * Cg + c];
-    acc.x += p.x;
-    acc.y += p.y;
-  }
-  red[threadIdx.x] = acc;
+  const int gi = blockIdx.x, b = blockIdx.y;
+  red[threadIdx.x] = fold_group_lane<false>(g, b, gi, threadIdx.x, kFoldThreads, BM, BN);
   __syncthreads();
-  for (int half = kFoldThreads / 2; half > 0; half >>= 1) {
-    if (threadIdx.x < half) {
-      red[threadIdx.x].x += red[threadIdx.x + half].x;
-      red[threadIdx.x].y += red[threadIdx.x + half].y;
-    }
-    __syncthreads();
-  }
   if (threadIdx.x == 0) {
-    out[(static_cast<int64_t>(b) * G + gi) * 2 + 0] = red[0].x;
-    out[(static_cast<int64_t>(b) * G + gi) * 2 + 1] = red[0].y;
+    float2 sum = red[0];
+    for (int q = 1; q < kFoldThreads; ++q) {
+      sum.x += red[q].x;
+      sum.y += red[q].y;
+    }
+    g.gsums[(static_cast<int64_t>(b) * g.G + gi) * 2] = sum.x;
+    g.gsums[(static_cast<int64_t>(b) * g.G + gi) * 2 + 1] = sum.y;
   }
 }
 
@@ -470,23 +611,31 @@ void launch_bf16(const GemmArgs& base, hipStream_t st) {
     hipLaunchKernelGGL((gemm_bf16<t.bm, t.bn, t.wgm, t.nw, kBK, kStages, t.occ, CONV>), grid, dim3(64 * t.nw), 0, st, g);
 }
 
-// Conv with GroupNorm partials: same tile choice, GNS epilogue, then the fold.
+// Conv with GroupNorm sums: same tile choice, GNS epilogue; the last tile of
+// each batch item folds its sums when the counters fit the fixed region and
+// the item's partials fit one block's fold, else a fold launch follows.
 template <int C>
-void launch_bf16_gns(const GemmArgs& base, float* sums, int G, hipStream_t st) {
+void launch_bf16_gns(const GemmArgs& base, hipStream_t st) {
   constexpr TileCfg t = kTiles[C];
   GemmArgs g = base;
   g.tiles_m = (g.M + t.bm - 1) / t.bm;
   g.tiles_n = (g.N + t.bn - 1) / t.bn;
   g.units = g.tiles_m * g.tiles_n;
   g.units_per_xcd = (g.units + kXcds - 1) / kXcds;
+  g.slots = (t.bn + g.Cg - 1) / g.Cg + 1;
+  const int64_t tiles_b = ((static_cast<int64_t>(g.gT) + t.bm - 1) / t.bm + 1) * g.tiles_n;
+  const int64_t B = g.M / g.gT;
+  g.counter_stride = static_cast<int>((1 + (tiles_b + kTicketGroup - 1) / kTicketGroup) * kCounterStride);
+  g.ticket = B * g.counter_stride * 4 <= kCounterBytes &&
+             tiles_b * g.slots * static_cast<int64_t>(sizeof(float2)) <= kTicketFoldBytes;
   const dim3 grid(static_cast<unsigned>(g.units_per_xcd * kXcds));
   if (g.K % t.bk == 0)
     hipLaunchKernelGGL((gemm_bf16<t.bm, t.bn, t.wgm, t.nw, t.bk, t.st, t.occ, true, true>), grid, dim3(64 * t.nw), 0, st, g);
   else
     hipLaunchKernelGGL((gemm_bf16<t.bm, t.bn, t.wgm, t.nw, kBK, kStages, t.occ, true, true>), grid, dim3(64 * t.nw), 0, st, g);
-  const int B = g.M / g.gT;
-  hipLaunchKernelGGL(gn_conv_fold, dim3(static_cast<unsigned>(G), static_cast<unsigned>(B)), dim3(kFoldThreads), 0, st,
-                     g.gpart, sums, g.N, G, g.gT, t.bm, t.wgm);
+  if (!g.ticket)
+    hipLaunchKernelGGL((gn_conv_fold<t.bm, t.bn>), dim3(static_cast<unsigned>(g.G), static_cast<unsigned>(B)),
+                       dim3(kFoldThreads), 0, st, g);
 }
 
 // Tile shape: fewest tiles per CU times tile area times the shape's cost per
@@ -727,11 +876,31 @@ DP_API dp_status dp_qkv_projection_into_buffers(const void* x, const void* wq, c
                   name);
 }
 
+namespace {
+// Workspace of the conv with GroupNorm sums: the fixed counter region, then the
+// (tile row, batch segment, tile column, group slot) partials, sized for every
+// tile shape the planner may pick and for one channel per group.
+struct ConvGnWs {
+  size_t partial_off, total;
+};
+ConvGnWs conv_gn_ws(int64_t B, int64_t h, int64_t W, int64_t Cout) {
+  const int64_t M = B * h * W;
+  int64_t part = 0;
+  for (const TileCfg& t : kTiles) {
+    const int64_t tm = (M + t.bm - 1) / t.bm, tn = (Cout + t.bn - 1) / t.bn;
+    part = std::max(part, tm * 2 * tn * (t.bn + 1));
+  }
+  ConvGnWs w{};
+  w.partial_off = kCounterBytes;
+  w.total = w.partial_off + static_cast<size_t>(part) * sizeof(float2);
+  return w;
+}
+}  // namespace
+
 DP_API size_t dp_conv3x3_gn_sums_workspace(int64_t B, int64_t h, int64_t W, int64_t Cout) {
   if (B <= 0 || h <= 0 || W <= 0 || Cout <= 0) return 0;
-  // partial rows: tiles_m * WGM <= M / (BM / WGM) + WGM, and BM / WGM >= 32
-  const int64_t rows = (B * h * W + 31) / 32 + 4;
-  return static_cast<size_t>(rows) * 2 * static_cast<size_t>(Cout) * sizeof(float2);
+  if (B * h * W > 0x7FFFFFFF || Cout > 0x7FFFFFFF) return 0;
+  return conv_gn_ws(B, h, W, Cout).total;
 }
 
 DP_API dp_status dp_conv3x3_stale_halo_gn_sums(const void* x, const void* halo_top, const void* halo_bot,
@@ -757,8 +926,9 @@ DP_API dp_status dp_conv3x3_stale_halo_gn_sums(const void* x, const void* halo_t
       dp::overlaps(gn_sums, sb, x, B * h * W * Cin * es) || dp::overlaps(gn_sums, sb, w, Cout * 9 * Cin * es) ||
       dp::overlaps(ws, need, x, B * h * W * Cin * es) || dp::overlaps(ws, need, w, Cout * 9 * Cin * es))
     return fail(DP_ERR_INVALID_ARG, "%s: an output overlaps an input or the workspace", name);
-  if (dt != DP_BF16 || Cin % kBK != 0 || Cin > 2048 || Cout % 32 != 0)
-    return fail(DP_ERR_UNSUPPORTED, "%s: needs bf16 with Cin %% 32 == 0, Cin <= 2048, Cout %% 32 == 0", name);
+  if (dt != DP_BF16 || Cin % kBK != 0 || Cin > 2048 || Cout % 32 != 0 || Cout > 2048)
+    return fail(DP_ERR_UNSUPPORTED, "%s: needs bf16 with Cin %% 32 == 0, Cin <= 2048, Cout %% 32 == 0, Cout <= 2048",
+                name);
   if (h * W < 160) return fail(DP_ERR_UNSUPPORTED, "%s: needs at least 160 tokens per batch item", name);
   if (B * h * W > 0x7FFFFFFF || 9 * Cin > 0x7FFFFFFF) return fail(DP_ERR_UNSUPPORTED, "%s: dimension exceeds 2^31", name);
   dp::clear_error();
@@ -770,16 +940,20 @@ DP_API dp_status dp_conv3x3_stale_halo_gn_sums(const void* x, const void* halo_t
   g.M = (int)(B * h * W);
   g.N = (int)Cout;
   g.K = (int)(9 * Cin);
-  g.gpart = static_cast<float2*>(ws);
+  const ConvGnWs lay = conv_gn_ws(B, h, W, Cout);
+  g.counters = static_cast<unsigned*>(ws);
+  g.gpart = reinterpret_cast<float2*>(static_cast<char*>(ws) + lay.partial_off);
+  g.gsums = gn_sums;
   g.gT = (int)(h * W);
-  const int Gi = (int)G;
+  g.G = (int)G;
+  g.Cg = (int)(Cout / G);
   switch (pick_tile(g)) {
-    case 0: launch_bf16_gns<0>(g, gn_sums, Gi, stream); break;
-    case 1: launch_bf16_gns<1>(g, gn_sums, Gi, stream); break;
-    case 2: launch_bf16_gns<2>(g, gn_sums, Gi, stream); break;
-    case 3: launch_bf16_gns<3>(g, gn_sums, Gi, stream); break;
-    case 4: launch_bf16_gns<4>(g, gn_sums, Gi, stream); break;
-    default: launch_bf16_gns<5>(g, gn_sums, Gi, stream); break;
+    case 0: launch_bf16_gns<0>(g, stream); break;
+    case 1: launch_bf16_gns<1>(g, stream); break;
+    case 2: launch_bf16_gns<2>(g, stream); break;
+    case 3: launch_bf16_gns<3>(g, stream); break;
+    case 4: launch_bf16_gns<4>(g, stream); break;
+    default: launch_bf16_gns<5>(g, stream); break;
   }
   return dp::check_launch(name);
 }

@@ -6,23 +6,24 @@
 // contrast) and the xDiT issue thread "Tensor Parallelism with Stale
 // Activations ..." (a feature may combine fresh partial values with stale ones).
 //
-// Two launches over the same (token tile, batch item) grid, deterministic
-// (fixed reduction order, no float atomics, no inter-block waiting):
-//   1. gn_partial: per tile, per group (sum x, sum x^2) -> workspace
-//   2. gn_apply:   every block folds the partials of its batch item in one
-//                  fixed order (so all blocks derive bit-identical statistics),
-//                  adds the other patches' stale sums and writes
-//                  y = x * a_c + b_c (a_c = rstd*gamma_c, b_c = beta_c - mean*a_c,
-//                  optional SiLU) for its tile; the block of tile 0 also writes
-//                  the fresh local sums.
-// Both launches use the same block -> tile mapping, so the tile block i
-// re-reads in pass 2 was read by block i, on the same XCD, in pass 1.
-//
-// A single pass that keeps each tile in registers while the blocks exchange
-// partials through device-scope atomics was measured slower on MI355X than
-// these two launches: the cross-XCD exchange (coherent stores, arrival
-// counter, uncached reads of every partial by every block) costs more than
-// re-reading x from the cache hierarchy.
+// Two launches, deterministic (fixed reduction order, no float atomics, no
+// block ever waits for another):
+//   1. gn_partial over (token tile, batch item): per tile and group (sum x,
+//      sum x^2) into the workspace; each block then takes a ticket, and the
+//      block that arrives last for its batch item folds that item's tile
+//      partials, in one fixed order, into the local sums [B, G, 2] (also the
+//      fresh sums the caller may ask for).  Tickets are two-level (16 blocks
+//      per first-level counter): on MI355X a single counter taken by ~500
+//      blocks costs ~5 us of contention, two levels ~1 us.
+//   2. gn_apply over its own, finer (token tile, batch item) grid: every block
+//      reads the local sums, adds the other patches' stale sums, derives
+//      a_c = rstd*gamma_c and b_c = beta_c - mean*a_c and writes
+//      y = x * a_c + b_c (optional SiLU) for its tile: a plain streaming pass.
+// The tile partials and the tickets cross XCDs inside one launch, so they are
+// written and read with device-coherent accesses (agent-scope atomic loads
+// and stores, which bypass the non-coherent per-XCD L2), ordered by a wait for
+// the stores' completion before the ticket.  The last arrivals put the
+// counters back to zero, so a workspace that starts zero-filled stays ready.
 //
 // Every thread owns one 16-byte channel vector of a token, so loads and stores
 // are 16 B wide and consecutive threads touch consecutive bytes.
@@ -33,24 +34,37 @@
 namespace {
 
 constexpr int kThreads = 512;
-constexpr int kTargetBlocks = 512;  // about two blocks per CU
+constexpr int kTargetBlocks = 512;  // sums pass: about two blocks per CU
 constexpr int kUnroll = 8;          // 16-byte loads in flight per thread
+constexpr int kApplyPasses = 8;     // apply pass: token passes per thread
+constexpr int kTicketGroup = 16;    // blocks per first-level ticket counter
+constexpr int kCounterStride = 32;  // uints between counters (one 128-byte line each)
+// Ticket counters live in a fixed region at the start of the workspace, the
+// same for every shape, and nothing else is ever written there: a workspace
+// zero-filled once stays valid for any sequence of calls.  A sums-pass launch
+// covers at most kMaxChunk batch items, so its counters always fit.
+constexpr int kCounterBytes = 32768;
+constexpr int kMaxChunk = 128;
 
 struct GnArgs {
   const void* x;
   void* y;
-  float2* partial;     // [B][tiles][G]
+  float2* partial;     // [B][tiles][G] (sums pass)
+  unsigned* counters;  // [B][1 + ticket groups] ticket counters, kCounterStride apart
+  float* sums;         // [B][G][2] the folded local sums (sums pass output)
   const float* stale;  // [n_patches][B][G][2]
   const float* gamma;
   const float* beta;
-  float* fresh;        // [B][G][2] or NULL
-  const float* given;  // [B][G][2] local sums computed elsewhere, or NULL (fold the partials)
-  int T, C, G, tiles, tile_tokens, n_patches, rank, B, silu;
+  float* fresh;        // [B][G][2] second copy of the local sums, or NULL
+  const float* given;  // [B][G][2] local sums the apply pass normalises with
+  float* coef;         // [Bc][2][C] per-channel (scale, shift) of the launch's batch items, or NULL
+  int T, C, G, tiles, tile_tokens, n_patches, rank, B, silu, counter_stride;
+  int b0;  // first batch item of the launch (blockIdx.y counts from it); B is the total
   float inv_count, eps;
 };
 
-// Upper bound of tiles per batch item, independent of C, dtype and device (it
-// sizes the workspace).
+// Upper bound of tiles per batch item of the sums pass, independent of C,
+// dtype and device (it sizes the workspace).
 int64_t max_tiles(int64_t B, int64_t T) {
   const int64_t want = (kTargetBlocks + B - 1) / B;
   return want < T ? want : T;
@@ -135,13 +149,35 @@ __device__ __forceinline__ void load_affine(const GnArgs& a, int vi, float* gm, 
   load_param(a.beta, vi * VEC, VEC, 0.f, bt);
 }
 
-// Block-wide per-group sums of the per-thread channel sums s1/s2, in a fixed
-// order: token lanes in order per channel, then channels in order per group.
-// lds_r holds [2][tpp*C] floats, lds_c [2][C]; the result lands in gsum[G].
-// Starts and ends with a barrier, so it may be called back to back.
+// Lanes per group for the block reductions below: a group's partial sums
+// are spread over `lanes` adjacent threads (so, when lanes <= 64, over lanes
+// of one wave, combined by a fixed shuffle tree).
+__device__ __forceinline__ int group_lanes(int G) {
+  int l = kThreads / G;
+  if (l > 64) l = 64;
+  if (l < 1) l = 1;
+  return 1 << (31 - __clz(l));  // a power of two
+}
+
+// Sum of v over `lanes` adjacent lanes (a power of two <= 64): a fixed xor
+// butterfly, so every lane ends with the same, order-fixed total.
+__device__ __forceinline__ float2 lane_sum(float2 v, int lanes) {
+  for (int off = 1; off < lanes; off <<= 1) {
+    v.x += __shfl_xor(v.x, off, 64);
+    v.y += __shfl_xor(v.y, off, 64);
+  }
+  return v;
+}
+
+// Block-wide per-group sums of the per-thread channel sums s1/s2 (thread =
+// token lane tl x channel vector vi), in a fixed order: lds_r holds
+// [2][tpp*C] floats; thread (g, j) of the group's `lanes` adds the entries
+// j, j + lanes, ... of the group's (token lane, channel) entries, eight LDS
+// reads in flight at a time, then the lanes are combined by lane_sum.  The
+// result lands in gsum[G].  Starts and ends with a barrier.
 template <int VEC>
 __device__ void block_group_sums(const float* s1, const float* s2, bool active, int tl, int vi,
-                                 int tpp, int C, int G, float* lds_r, float* lds_c, float2* gsum) {
+                                 int tpp, int C, int G, float* lds_r, float2* gsum) {
   __syncthreads();
   if (active) {
 #pragma unroll
@@ -151,39 +187,59 @@ __device__ void block_group_sums(const float* s1, const float* s2, bool active, 
     }
   }
   __syncthreads();
-  for (int c = threadIdx.x; c < C; c += kThreads) {
-    float p1 = 0.f, p2 = 0.f;
-    for (int k = 0; k < tpp; ++k) {
-      p1 += lds_r[k * C + c];
-      p2 += lds_r[tpp * C + k * C + c];
+  const int lanes = group_lanes(G), Cg = C / G, n = tpp * Cg;
+  constexpr int U = 8;
+  for (int f = threadIdx.x; f < ((G * lanes + 63) / 64) * 64; f += kThreads) {
+    const int g = f / lanes, j = f % lanes;
+    float2 acc = make_float2(0.f, 0.f);
+    if (g < G) {
+      for (int e0 = j; e0 < n; e0 += U * lanes) {
+        float v1[U], v2[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int e = min(e0 + u * lanes, n - 1);
+          const int idx = (e / Cg) * C + g * Cg + e % Cg;
+          v1[u] = lds_r[idx];
+          v2[u] = lds_r[tpp * C + idx];
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          if (e0 + u * lanes < n) {
+            acc.x += v1[u];
+            acc.y += v2[u];
+          }
+        }
+      }
     }
-    lds_c[c] = p1;
-    lds_c[C + c] = p2;
-  }
-  __syncthreads();
-  const int Cg = C / G;
-  for (int g = threadIdx.x; g < G; g += kThreads) {
-    float p1 = 0.f, p2 = 0.f;
-    for (int c = g * Cg; c < (g + 1) * Cg; ++c) {
-      p1 += lds_c[c];
-      p2 += lds_c[C + c];
-    }
-    gsum[g] = make_float2(p1, p2);
+    acc = lane_sum(acc, lanes);
+    if (g < G && j == 0) gsum[g] = acc;
   }
   __syncthreads();
 }
 
-// Folds the tile partials of batch item b into lane sums red[q*G + g] (lane q
-// takes tiles q, q + lanes, ..., U per pass in U accumulators); returns the
-// lane count.  A pass issues all U loads before it adds any of them (indexes
-// past the last tile re-read that tile and are not added), so one memory
-// round trip covers up to U * lanes tiles.  One fixed order, so every block
-// (and dp_groupnorm_sums) derives bit-identical sums.
-__device__ int fold_partials(const GnArgs& a, int b, float2* red) {
-  const int G = a.G;
-  const int lanes = G >= kThreads ? 1 : kThreads / G;
+// Device-coherent 8-byte store and load (agent scope: they bypass the per-XCD
+// L2, so blocks on other XCDs see them within the same launch).
+__device__ __forceinline__ void store_coherent(float2* p, float2 v) {
+  __hip_atomic_store(reinterpret_cast<unsigned long long*>(p), __builtin_bit_cast(unsigned long long, v),
+                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float2 load_coherent(const float2* p) {
+  return __builtin_bit_cast(float2, __hip_atomic_load(reinterpret_cast<const unsigned long long*>(p),
+                                                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+}
+
+// Folds the tile partials of batch item b into red[g] (float2 per group).
+// The loads are coalesced: thread f = q * G + g takes group g of tiles q,
+// q + lanes, ..., U loads in flight per pass (indexes past the last tile
+// re-read that tile and are not added); its sum goes to red[f], and after a
+// barrier the group's `lanes` sums are combined by lane_sum over adjacent
+// threads.  One fixed order, whichever block runs it.  red holds
+// lanes * G float2.  Starts and ends with a barrier.
+__device__ void fold_partials(const GnArgs& a, int b, float2* red) {
+  const int G = a.G, lanes = group_lanes(G);
   const float2* pb = a.partial + static_cast<int64_t>(b) * a.tiles * G;
   constexpr int U = 16;
+  __syncthreads();
   for (int f = threadIdx.x; f < lanes * G; f += kThreads) {
     const int g = f % G, q = f / G;
     float2 acc[U];
@@ -192,7 +248,8 @@ __device__ int fold_partials(const GnArgs& a, int b, float2* red) {
     for (int t0 = q; t0 < a.tiles; t0 += U * lanes) {
       float2 v[U];
 #pragma unroll
-      for (int u = 0; u < U; ++u) v[u] = pb[static_cast<int64_t>(min(t0 + u * lanes, a.tiles - 1)) * G + g];
+      for (int u = 0; u < U; ++u)
+        v[u] = load_coherent(pb + static_cast<int64_t>(min(t0 + u * lanes, a.tiles - 1)) * G + g);
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         if (t0 + u * lanes < a.tiles) {
@@ -209,103 +266,111 @@ __device__ int fold_partials(const GnArgs& a, int b, float2* red) {
     }
     red[f] = s;
   }
-  return lanes;
-}
-
-// The first kStalePre patches' stale sums of group g of batch item b, loaded
-// ahead of the fold so that their latency overlaps it (the thread of group g
-// finalises that group).
-constexpr int kStalePre = 8;
-struct StalePre {
-  float2 v[kStalePre];
-};
-
-__device__ __forceinline__ StalePre prefetch_stale(const GnArgs& a, int b, int g) {
-  StalePre sp;
-#pragma unroll
-  for (int j = 0; j < kStalePre; ++j) sp.v[j] = make_float2(0.f, 0.f);
-  if (g < a.G && a.n_patches > 1) {
-#pragma unroll
-    for (int j = 0; j < kStalePre; ++j) {
-      const float* st = a.stale + ((static_cast<int64_t>(min(j, a.n_patches - 1)) * a.B + b) * a.G + g) * 2;
-      sp.v[j] = make_float2(st[0], st[1]);
-    }
+  __syncthreads();
+  float2 mine[(2048 + kThreads - 1) / kThreads];
+  int k = 0;
+  for (int f = threadIdx.x; f < ((G * lanes + 63) / 64) * 64; f += kThreads, ++k) {
+    const int g = f / lanes, q = f % lanes;
+    const float2 v = lane_sum(g < G ? red[q * G + g] : make_float2(0.f, 0.f), lanes);
+    mine[k] = v;
   }
-  return sp;
+  __syncthreads();
+  k = 0;
+  for (int f = threadIdx.x; f < ((G * lanes + 63) / 64) * 64; f += kThreads, ++k) {
+    const int g = f / lanes, q = f % lanes;
+    if (g < G && q == 0) red[g] = mine[k];
+  }
+  __syncthreads();
 }
 
-// Statistics of batch item b from the lane sums red[q*G + g] (lanes in
-// order): fresh local sums out (tile 0 only), stale sums of the other
-// patches added in patch order (the first kStalePre from `pre`, prefetched by
-// the thread of group g = threadIdx.x), (mean, rstd) per group into gstat.
-__device__ void finalize_stats(const GnArgs& a, int b, int tile, int lanes, const float2* red,
-                               const StalePre& pre, float2* gstat) {
-  const int G = a.G;
-  for (int g = threadIdx.x; g < G; g += kThreads) {
-    float f1 = 0.f, f2 = 0.f;
-    for (int q = 0; q < lanes; ++q) {
-      f1 += red[q * G + g].x;
-      f2 += red[q * G + g].y;
-    }
-    if (tile == 0 && a.fresh) {
-      a.fresh[(static_cast<int64_t>(b) * G + g) * 2 + 0] = f1;
-      a.fresh[(static_cast<int64_t>(b) * G + g) * 2 + 1] = f2;
-    }
-    if (g == static_cast<int>(threadIdx.x)) {
+// (mean, rstd) of one group from its sums over the image (biased variance,
+// clamped at zero since stale remote sums can make it negative), and a
+// channel's (scale, shift) from them.  Explicit fused operations, so every
+// kernel that calls these rounds identically.
+__device__ __forceinline__ float2 group_stats(float f1, float f2, float inv_count, float eps) {
+  const float mean = f1 * inv_count;
+  const float var = fmaxf(fmaf(-mean, mean, f2 * inv_count), 0.f);
+  return make_float2(mean, 1.0f / sqrtf(var + eps));
+}
+__device__ __forceinline__ float2 channel_affine(float2 ms, float gamma, float beta) {
+  const float sc = ms.y * gamma;
+  return make_float2(sc, fmaf(-ms.x, sc, beta));
+}
+
+// Patches from p_start on are taken eight at a time, all eight loads in
+// flight before any is added.
+__device__ __forceinline__ float2 add_stale(const GnArgs& a, float2 loc, int gb, int g, int p_start) {
+  constexpr int U = 8;
+  for (int p0 = p_start; p0 < a.n_patches; p0 += U) {
+    float2 v[U];
 #pragma unroll
-      for (int j = 0; j < kStalePre; ++j) {
-        if (j < a.n_patches && j != a.rank) {
-          f1 += pre.v[j].x;
-          f2 += pre.v[j].y;
-        }
+    for (int u = 0; u < U; ++u) {
+      const float* st = a.stale + ((static_cast<int64_t>(min(p0 + u, a.n_patches - 1)) * a.B + gb) * a.G + g) * 2;
+      v[u] = make_float2(st[0], st[1]);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (p0 + u < a.n_patches && p0 + u != a.rank) {
+        loc.x += v[u].x;
+        loc.y += v[u].y;
       }
     }
-    for (int p = g == static_cast<int>(threadIdx.x) ? kStalePre : 0; p < a.n_patches; ++p) {
-      if (p == a.rank) continue;
-      const float* st = a.stale + ((static_cast<int64_t>(p) * a.B + b) * G + g) * 2;
-      f1 += st[0];
-      f2 += st[1];
+  }
+  return loc;
+}
+__device__ __forceinline__ float2 image_sums(const GnArgs& a, float2 loc, int gb, int g) {
+  return add_stale(a, loc, gb, g, 0);
+}
+
+// The first kStalePre patches' stale sums of group g, loaded ahead so that
+// their latency overlaps other loads; added in patch order by stale_prefix.
+constexpr int kStalePre = 8;
+__device__ __forceinline__ void prefetch_stale(const GnArgs& a, int gb, int g, float2* pre) {
+#pragma unroll
+  for (int j = 0; j < kStalePre; ++j) {
+    const float* st = a.stale + ((static_cast<int64_t>(min(j, a.n_patches - 1)) * a.B + gb) * a.G + g) * 2;
+    pre[j] = a.n_patches > 1 ? make_float2(st[0], st[1]) : make_float2(0.f, 0.f);
+  }
+}
+__device__ __forceinline__ float2 stale_prefix(const GnArgs& a, float2 f, const float2* pre) {
+#pragma unroll
+  for (int j = 0; j < kStalePre; ++j) {
+    if (j < a.n_patches && j != a.rank) {
+      f.x += pre[j].x;
+      f.y += pre[j].y;
     }
-    const float mean = f1 * a.inv_count;
-    const float var = fmaxf(f2 * a.inv_count - mean * mean, 0.f);
-    gstat[g] = make_float2(mean, 1.0f / sqrtf(var + a.eps));
   }
+  return f;
 }
 
-template <int VEC>
-__device__ __forceinline__ void channel_coeffs(const float2* gstat, int vi, int Cg, const float* gm,
-                                               const float* bt, float* ca, float* cb) {
-#pragma unroll
-  for (int j = 0; j < VEC; ++j) {
-    const float2 ms = gstat[(vi * VEC + j) / Cg];
-    ca[j] = ms.y * gm[j];
-    cb[j] = bt[j] - ms.x * ca[j];
-  }
-}
-
-template <bool BF16>
-__device__ __forceinline__ void normalize_store(const GnArgs& a, int b, int t, int vi, const u32x4& u,
-                                                const float* ca, const float* cb) {
-  constexpr int VEC = BF16 ? 8 : 4;
-  float v[VEC];
-  unpack_vec<BF16>(u, v);
-#pragma unroll
-  for (int j = 0; j < VEC; ++j) {
-    float z = fmaf(v[j], ca[j], cb[j]);
-    if (a.silu) z *= __builtin_amdgcn_rcpf(1.0f + __expf(-z));  // v_rcp_f32, 1 ulp
-    v[j] = z;
-  }
-  __builtin_nontemporal_store(
-      pack_vec<BF16>(v), reinterpret_cast<u32x4*>(static_cast<char*>(a.y) + vec_byte<BF16>(b, t, vi, a)));
+// ------------------------------------------------------------ tickets
+// Counts block `tile` of batch item b in; true for exactly one block, the last
+// of the item's `tiles` to arrive.  First-level counters take kTicketGroup
+// blocks each, the item's top counter one arrival per group.  Every counter is
+// back at zero once all blocks of the launch have arrived.
+__device__ bool take_ticket(const GnArgs& a, int b, int tile) {
+  unsigned* base = a.counters + static_cast<int64_t>(b) * a.counter_stride;
+  const int grp = tile / kTicketGroup;
+  const unsigned in_grp = static_cast<unsigned>(min(kTicketGroup, a.tiles - grp * kTicketGroup));
+  const unsigned n_grp = static_cast<unsigned>((a.tiles + kTicketGroup - 1) / kTicketGroup);
+  unsigned* gc = base + (1 + grp) * kCounterStride;
+  if (__hip_atomic_fetch_add(gc, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != in_grp - 1) return false;
+  __hip_atomic_store(gc, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (__hip_atomic_fetch_add(base, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != n_grp - 1) return false;
+  __hip_atomic_store(base, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return true;
 }
 
 // ------------------------------------------------------------ kernels
+// Sums pass: tile partials, then the last block of each batch item folds them
+// into a.sums (and a.fresh when given).
 template <bool BF16>
 __global__ void __launch_bounds__(kThreads) gn_partial(GnArgs a) {
   constexpr int VEC = BF16 ? 8 : 4;
   __shared__ float lds_r[2 * kThreads * VEC];
   __shared__ float lds_c[2 * 2048];
   __shared__ float2 gsum[2048];
+  __shared__ int last;
   const int vpt = a.C / VEC, tpp = kThreads / vpt;
   const int tid = threadIdx.x, tl = tid / vpt, vi = tid % vpt;
   const bool active = tl < tpp;
@@ -327,95 +392,199 @@ __global__ void __launch_bounds__(kThreads) gn_partial(GnArgs a) {
     for (int u = 0; u < kUnroll; ++u)
       if (k0 + u < npass) acc_vec<BF16>(raw[u], s1, s2);
   }
-  block_group_sums<VEC>(s1, s2, active, tl, vi, tpp, a.C, a.G, lds_r, lds_c, gsum);
+  block_group_sums<VEC>(s1, s2, active, tl, vi, tpp, a.C, a.G, lds_r, gsum);
   for (int g = tid; g < a.G; g += kThreads)
-    a.partial[(static_cast<int64_t>(b) * a.tiles + tile) * a.G + g] = gsum[g];
+    store_coherent(a.partial + (static_cast<int64_t>(b) * a.tiles + tile) * a.G + g, gsum[g]);
+  // the block's partials are complete at the coherence point before its ticket
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (tid == 0) last = take_ticket(a, b, tile);
+  __syncthreads();
+  if (!last) return;
+  // the coefficient table's inputs (the group's first stale sums, the
+  // channels' gamma/beta) go out together with the fold's loads
+  const int gb = a.b0 + b;
+  float2 pre[kStalePre];
+  constexpr int kCpt = 2048 / kThreads;  // channels per thread, C <= 2048
+  float gpre[kCpt], bpre[kCpt];
+  if (a.coef) {
+    if (tid < a.G) prefetch_stale(a, gb, tid, pre);
+#pragma unroll
+    for (int k = 0; k < kCpt; ++k) {
+      const int c = min(tid + k * kThreads, a.C - 1);
+      gpre[k] = a.gamma ? a.gamma[c] : 1.f;
+      bpre[k] = a.beta ? a.beta[c] : 0.f;
+    }
+  }
+  fold_partials(a, b, gsum);
+  __syncthreads();
+  float2* ms = reinterpret_cast<float2*>(lds_c);  // [G] (mean, rstd)
+  for (int g = tid; g < a.G; g += kThreads) {
+    const float f1 = gsum[g].x, f2 = gsum[g].y;
+    const int64_t o = (static_cast<int64_t>(b) * a.G + g) * 2;
+    if (a.sums) {
+      a.sums[o] = f1;
+      a.sums[o + 1] = f2;
+    }
+    if (a.fresh) {
+      a.fresh[o] = f1;
+      a.fresh[o + 1] = f2;
+    }
+    if (a.coef) {
+      float2 f = make_float2(f1, f2);
+      f = g == tid ? add_stale(a, stale_prefix(a, f, pre), gb, g, kStalePre) : image_sums(a, f, gb, g);
+      ms[g] = group_stats(f.x, f.y, a.inv_count, a.eps);
+    }
+  }
+  if (!a.coef) return;
+  __syncthreads();
+  const int Cg = a.C / a.G;
+  float* cf = a.coef + static_cast<int64_t>(b) * 2 * a.C;
+#pragma unroll
+  for (int k = 0; k < kCpt; ++k) {
+    const int c = tid + k * kThreads;
+    if (c < a.C) {
+      const float2 af = channel_affine(ms[c / Cg], gpre[k], bpre[k]);
+      cf[c] = af.x;
+      cf[a.C + c] = af.y;
+    }
+  }
 }
 
-template <bool BF16>
-__global__ void __launch_bounds__(kThreads) gn_apply(GnArgs a) {
+// Apply passes: y = x * scale_c + shift_c (SiLU optional) over a tile of
+// tokens.  A thread owns one 16-byte channel vector of kApplyPasses tokens
+// (tokens tl, tl + tpp, ...), issues all its loads at once and stores with
+// nontemporal 16-byte writes.
+// SILU is a template parameter: a runtime branch would have the compiler
+// evaluate the SiLU's two transcendentals for every element and then select.
+template <bool BF16, bool SILU>
+__device__ __forceinline__ void apply_store(const GnArgs& a, const u32x4* raw, int64_t base, int stride_vec,
+                                            int n, const float* sc, const float* sh) {
   constexpr int VEC = BF16 ? 8 : 4;
-  __shared__ float2 red[2048];    // [lanes][G], lanes * G <= max(G, kThreads)
-  __shared__ float2 gstat[2048];  // (mean, rstd) per group
-  const int G = a.G;
-  const int vpt = a.C / VEC, tpp = kThreads / vpt;
-  const int tid = threadIdx.x, tl = tid / vpt, vi = tid % vpt;
-  const bool active = tl < tpp;
-  const int b = blockIdx.y, tile = blockIdx.x;
-  const int t_begin = tile * a.tile_tokens;
-  const int t_end = min(a.T, t_begin + a.tile_tokens);
-  const int npass = a.tile_tokens / tpp;
-
-  // gamma/beta and the first loads of the tile go out before the fold, which
-  // then runs under their latency
-  float gm[VEC], bt[VEC];
-  if (active) load_affine<VEC>(a, vi, gm, bt);
-  u32x4 first[kUnroll];
 #pragma unroll
-  for (int u = 0; u < kUnroll; ++u)
-    first[u] = load_or_zero<BF16>(a, b, t_begin + tl + u * tpp, t_end, vi, active && u < npass);
-
-  const StalePre pre = prefetch_stale(a, b, tid);
-  int lanes = 1;
-  if (a.given) {  // the local sums come from the caller: one lane holding them
-    for (int g = tid; g < G; g += kThreads)
-      red[g] = make_float2(a.given[(static_cast<int64_t>(b) * G + g) * 2], a.given[(static_cast<int64_t>(b) * G + g) * 2 + 1]);
-  } else {
-    lanes = fold_partials(a, b, red);
-  }
-  __syncthreads();
-  finalize_stats(a, b, tile, lanes, red, pre, gstat);
-  __syncthreads();
-
-  if (!active) return;
-  float ca[VEC], cb[VEC];
-  channel_coeffs<VEC>(gstat, vi, a.C / G, gm, bt, ca, cb);
-  if (npass <= kUnroll) {  // one group of passes: its loads went out before the fold
+  for (int u = 0; u < kApplyPasses; ++u) {
+    if (u >= n) break;
+    float v[VEC];
+    unpack_vec<BF16>(raw[u], v);
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int t = t_begin + tl + u * tpp;
-      if (u < npass && t < t_end) normalize_store<BF16>(a, b, t, vi, first[u], ca, cb);
+    for (int j = 0; j < VEC; ++j) {
+      float z = fmaf(v[j], sc[j], sh[j]);
+      if constexpr (SILU) z *= __builtin_amdgcn_rcpf(1.0f + __expf(-z));  // v_rcp_f32, 1 ulp
+      v[j] = z;
     }
-    return;
-  }
-  // double-buffered: the loads of the next kUnroll passes go out before this
-  // group's normalise-and-store, so reads and writes stay in flight together
-  u32x4 cur[kUnroll];
-#pragma unroll
-  for (int u = 0; u < kUnroll; ++u) cur[u] = first[u];
-  for (int k0 = 0; k0 < npass; k0 += kUnroll) {
-    u32x4 nxt[kUnroll];
-    const bool more = k0 + kUnroll < npass;
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u)
-      nxt[u] = load_or_zero<BF16>(a, b, t_begin + tl + (k0 + kUnroll + u) * tpp, t_end, vi,
-                                  more && k0 + kUnroll + u < npass);
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int t = t_begin + tl + (k0 + u) * tpp;
-      if (k0 + u < npass && t < t_end) normalize_store<BF16>(a, b, t, vi, cur[u], ca, cb);
-    }
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) cur[u] = nxt[u];
+    __builtin_nontemporal_store(pack_vec<BF16>(v), static_cast<u32x4*>(a.y) + base + static_cast<int64_t>(u) * stride_vec);
   }
 }
 
-// Local sums only: one block per batch item folds the partials (in the order
-// gn_apply uses) and writes (sum x, sum x^2) per group.
-__global__ void __launch_bounds__(kThreads) gn_sums(GnArgs a) {
-  __shared__ float2 red[2048];
-  const int b = blockIdx.y, G = a.G;
-  const int lanes = fold_partials(a, b, red);
-  __syncthreads();
-  for (int g = threadIdx.x; g < G; g += kThreads) {
-    float f1 = 0.f, f2 = 0.f;
-    for (int q = 0; q < lanes; ++q) {
-      f1 += red[q * G + g].x;
-      f2 += red[q * G + g].y;
+// The thread's tokens: n of them, starting at vector index `base` of x/y
+// (16-byte units), stride_vec apart.
+template <bool BF16, int NT>
+__device__ __forceinline__ bool apply_slot(const GnArgs& a, int& vi, int64_t& base, int& stride_vec, int& n) {
+  constexpr int VEC = BF16 ? 8 : 4;
+  const int vpt = a.C / VEC, tpp = NT / vpt;
+  const int tl = threadIdx.x / vpt;
+  vi = threadIdx.x - tl * vpt;
+  if (tl >= tpp) return false;
+  const int t = blockIdx.x * a.tile_tokens + tl;
+  n = t < a.T ? min(kApplyPasses, (a.T - t + tpp - 1) / tpp) : 0;
+  base = (static_cast<int64_t>(blockIdx.y) * a.T + t) * vpt + vi;
+  stride_vec = tpp * vpt;
+  return true;
+}
+
+// Two-pass GroupNorm, second pass: the channel coefficients come from the
+// table the sums pass wrote.
+template <bool BF16, int NT, bool SILU>
+__global__ void __launch_bounds__(NT) gn_apply_table(GnArgs a) {
+  constexpr int VEC = BF16 ? 8 : 4;
+  int vi, stride_vec, n;
+  int64_t base;
+  if (!apply_slot<BF16, NT>(a, vi, base, stride_vec, n)) return;
+  u32x4 raw[kApplyPasses];
+  const u32x4* x = static_cast<const u32x4*>(a.x);
+#pragma unroll
+  for (int u = 0; u < kApplyPasses; ++u) raw[u] = u < n ? x[base + static_cast<int64_t>(u) * stride_vec] : u32x4{0u, 0u, 0u, 0u};
+  const float* cf = a.coef + static_cast<int64_t>(blockIdx.y) * 2 * a.C + vi * VEC;
+  float sc[VEC], sh[VEC];
+#pragma unroll
+  for (int j = 0; j < VEC; j += 4) {
+    const f32x4 s4 = *reinterpret_cast<const f32x4*>(cf + j), h4 = *reinterpret_cast<const f32x4*>(cf + a.C + j);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      sc[j + e] = s4[e];
+      sh[j + e] = h4[e];
     }
-    a.fresh[(static_cast<int64_t>(b) * G + g) * 2 + 0] = f1;
-    a.fresh[(static_cast<int64_t>(b) * G + g) * 2 + 1] = f2;
   }
+  apply_store<BF16, SILU>(a, raw, base, stride_vec, n, sc, sh);
+}
+
+// GroupNorm from given local sums: the block stages its batch item's local
+// sums and the other patches' stale sums in LDS (a few loads per thread,
+// issued before the x loads, so the barrier waits for them only); thread g
+// then derives group g's (mean, rstd) with the arithmetic the sums pass uses
+// for its table (local sums, then the patches in order: both entry points
+// give bit-identical outputs), and after a second barrier every thread reads
+// its channels' statistics.  Stale sums beyond kStaleLds entries are read
+// from memory by thread g instead.
+constexpr int kStaleLds = 1024;  // float2 entries: patches * G
+template <bool BF16, int NT, bool SILU>
+__global__ void __launch_bounds__(NT) gn_apply_sums(GnArgs a) {
+  constexpr int VEC = BF16 ? 8 : 4;
+  __shared__ float2 st_lds[kStaleLds];  // [n_patches][G] stale sums
+  __shared__ float2 g_lds[2048];        // [G] local sums, then (mean, rstd)
+  int vi = 0, stride_vec = 0, n = 0;
+  int64_t base = 0;
+  const bool on = apply_slot<BF16, NT>(a, vi, base, stride_vec, n);
+  const int G = a.G, Cg = a.C / G, gb = a.b0 + blockIdx.y;
+  const bool staged = a.n_patches * G <= kStaleLds;
+  const float* loc = a.given + static_cast<int64_t>(blockIdx.y) * G * 2;
+  for (int f = threadIdx.x; f < G; f += NT) g_lds[f] = make_float2(loc[f * 2], loc[f * 2 + 1]);
+  if (staged && a.n_patches > 1) {
+    for (int f = threadIdx.x; f < a.n_patches * G; f += NT) {
+      const int p = f / G, g = f - p * G;
+      const float* st = a.stale + ((static_cast<int64_t>(p) * a.B + gb) * G + g) * 2;
+      st_lds[f] = make_float2(st[0], st[1]);
+    }
+  }
+  float gm[VEC], bt[VEC];
+  if (on) load_affine<VEC>(a, vi, gm, bt);
+  u32x4 raw[kApplyPasses];
+  const u32x4* x = static_cast<const u32x4*>(a.x);
+#pragma unroll
+  for (int u = 0; u < kApplyPasses; ++u)
+    raw[u] = on && u < n ? x[base + static_cast<int64_t>(u) * stride_vec] : u32x4{0u, 0u, 0u, 0u};
+  __syncthreads();
+  for (int g = threadIdx.x; g < G; g += NT) {
+    float2 f = g_lds[g];
+    if (staged) {
+      constexpr int U = 8;
+      for (int p0 = 0; p0 < a.n_patches; p0 += U) {
+        float2 v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) v[u] = st_lds[min(p0 + u, a.n_patches - 1) * G + g];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          if (p0 + u < a.n_patches && p0 + u != a.rank) {
+            f.x += v[u].x;
+            f.y += v[u].y;
+          }
+        }
+      }
+    } else {
+      f = add_stale(a, f, gb, g, 0);
+    }
+    g_lds[g] = group_stats(f.x, f.y, a.inv_count, a.eps);
+  }
+  __syncthreads();
+  if (!on) return;
+  float sc[VEC], sh[VEC];
+#pragma unroll
+  for (int j = 0; j < VEC; ++j) {
+    const float2 af = channel_affine(g_lds[(vi * VEC + j) / Cg], gm[j], bt[j]);
+    sc[j] = af.x;
+    sh[j] = af.y;
+  }
+  apply_store<BF16, SILU>(a, raw, base, stride_vec, n, sc, sh);
 }
 
 // ------------------------------------------------------------ planning
@@ -423,29 +592,168 @@ struct GnPlan {
   int tile_tokens, tiles;
 };
 
-// Tokens per tile: a whole number of block passes (tpp tokens each); at most
-// max_tiles(B, T) tiles per batch item.
-GnPlan make_plan(int64_t B, int64_t T, int64_t C, dp_dtype dt) {
-  const int vec = dt == DP_BF16 ? 8 : 4;
-  const int tpp = kThreads / static_cast<int>(C / vec);
+// Sums pass: tokens per tile a whole number of block passes (tpp tokens each),
+// at most max_tiles(B, T) tiles per batch item.
+int tokens_per_pass(int64_t C, dp_dtype dt) { return kThreads / static_cast<int>(C / (dt == DP_BF16 ? 8 : 4)); }
+
+GnPlan sums_plan(int64_t B, int64_t T, int64_t C, dp_dtype dt) {
+  const int tpp = tokens_per_pass(C, dt);
   const int64_t per_b = max_tiles(B, T);
   int64_t tt = (T + per_b - 1) / per_b;
   tt = (tt + tpp - 1) / tpp * tpp;
   return GnPlan{static_cast<int>(tt), static_cast<int>((T + tt - 1) / tt)};
 }
 
-// Workspace: the per-tile partials [B][max_tiles][G] of float2.
-size_t workspace_bytes(int64_t B, int64_t T, int64_t G) {
-  return static_cast<size_t>(B) * static_cast<size_t>(max_tiles(B, T)) * static_cast<size_t>(G) *
-         sizeof(float2);
+// Apply pass: blocks of 256 threads (512 when a token has more than 256
+// channel vectors), kApplyPasses block passes per tile.
+int apply_threads(int64_t C, dp_dtype dt) { return C / (dt == DP_BF16 ? 8 : 4) <= 256 ? 256 : 512; }
+GnPlan apply_plan(int64_t T, int64_t C, dp_dtype dt) {
+  const int64_t tpp = apply_threads(C, dt) / (C / (dt == DP_BF16 ? 8 : 4));
+  const int64_t tt = tpp * kApplyPasses;
+  return GnPlan{static_cast<int>(tt), static_cast<int>((T + tt - 1) / tt)};
+}
+
+// Workspace: the fixed counter region, then for one launch of up to
+// kMaxChunk batch items the folded sums and the tile partials.
+struct GnWs {
+  size_t sums_off, coef_off, partial_off, total;
+  int counter_stride;  // uints per batch item
+};
+size_t round256(size_t n) { return (n + 255) / 256 * 256; }
+GnWs ws_layout(int64_t B, int64_t T, int64_t C, int64_t G) {
+  const int64_t Bc = std::min<int64_t>(B, kMaxChunk);
+  GnWs w{};
+  const int64_t groups = (max_tiles(Bc, T) + kTicketGroup - 1) / kTicketGroup;
+  w.counter_stride = static_cast<int>((1 + groups) * kCounterStride);
+  w.sums_off = kCounterBytes;
+  w.coef_off = w.sums_off + round256(static_cast<size_t>(Bc) * G * 2 * sizeof(float));
+  w.partial_off = w.coef_off + round256(static_cast<size_t>(Bc) * C * 2 * sizeof(float));
+  w.total = w.partial_off + static_cast<size_t>(Bc) * max_tiles(Bc, T) * G * sizeof(float2);
+  return w;
+}
+// Bytes for a call over B batch items: the largest chunk layout it uses.
+size_t ws_bytes(int64_t B, int64_t T, int64_t C, int64_t G) {
+  size_t n = ws_layout(std::min<int64_t>(B, kMaxChunk), T, C, G).total;
+  if (B > kMaxChunk && B % kMaxChunk) n = std::max(n, ws_layout(B % kMaxChunk, T, C, G).total);
+  return n;
+}
+// With at most kMaxChunk batch items per launch, Bc * (1 + ceil(tiles / 16))
+// counter lines never exceed the region: checked for every chunk size.
+static_assert(kMaxChunk * (1 + ((kTargetBlocks + kMaxChunk - 1) / kMaxChunk + kTicketGroup - 1) / kTicketGroup) *
+                      kCounterStride * 4 <= kCounterBytes,
+              "counter region");
+
+// Checks shared by the GroupNorm calls; fills the shape fields of `ga`.
+dp_status check_common(const char* name, const void* x, int64_t B, int64_t T_loc, int64_t C, int64_t G,
+                       dp_dtype dt, GnArgs& ga) {
+  using dp::fail;
+  if (!x) return fail(DP_ERR_INVALID_ARG, "%s: NULL x", name);
+  if (B <= 0 || T_loc <= 0 || C <= 0 || G <= 0) return fail(DP_ERR_INVALID_ARG, "%s: sizes must be positive", name);
+  if (C % G != 0) return fail(DP_ERR_INVALID_ARG, "%s: C %% G != 0", name);
+  if (!dp::dtype_ok(dt)) return fail(DP_ERR_INVALID_ARG, "%s: bad dtype", name);
+  const int vec = dt == DP_BF16 ? 8 : 4;
+  if (C % vec != 0 || C > 2048 || C / vec > kThreads || T_loc > 0x7FFFFFFF || B > 65535 || B * G > 0x7FFFFFFF)
+    return fail(DP_ERR_UNSUPPORTED, "%s: C=%lld G=%lld not supported", name, (long long)C, (long long)G);
+  ga.x = x;
+  ga.T = static_cast<int>(T_loc);
+  ga.C = static_cast<int>(C);
+  ga.G = static_cast<int>(G);
+  ga.B = static_cast<int>(B);
+  return DP_OK;
+}
+
+dp_status check_stats_args(const char* name, const float* stale_sums, int64_t n_patches, int64_t rank,
+                           int64_t T_total, int64_t T_loc, float eps) {
+  using dp::fail;
+  if (n_patches <= 0) return fail(DP_ERR_INVALID_ARG, "%s: n_patches must be positive", name);
+  if (!stale_sums && n_patches > 1)
+    return fail(DP_ERR_INVALID_ARG, "%s: NULL stale_sums with %lld patches", name, (long long)n_patches);
+  if (rank < 0 || rank >= n_patches)
+    return fail(DP_ERR_INVALID_ARG, "%s: rank %lld outside [0, %lld)", name, (long long)rank, (long long)n_patches);
+  if (T_total < T_loc) return fail(DP_ERR_INVALID_ARG, "%s: T_total < T_loc", name);
+  if (!(eps >= 0.f)) return fail(DP_ERR_INVALID_ARG, "%s: eps must be >= 0", name);
+  return DP_OK;
+}
+
+void set_stats(GnArgs& ga, const float* stale_sums, int64_t n_patches, int64_t rank, int64_t T_total,
+               const float* gamma, const float* beta, float eps, int fuse_silu) {
+  ga.stale = stale_sums;
+  ga.gamma = gamma;
+  ga.beta = beta;
+  ga.n_patches = static_cast<int>(n_patches);
+  ga.rank = static_cast<int>(rank);
+  ga.silu = fuse_silu;
+  ga.inv_count = static_cast<float>(1.0 / (static_cast<double>(T_total) * (ga.C / ga.G)));
+  ga.eps = eps;
+}
+
+// Sums pass over batch items [b0, b0 + Bc) of the call (Bc <= kMaxChunk):
+// local sums into the workspace (and `fresh`, already offset to b0) and,
+// when `table` is set, the apply pass's coefficient table.
+void launch_sums(GnArgs ga, int b0, int Bc, void* ws, float* fresh, bool table, dp_dtype dt, hipStream_t st) {
+  const GnWs w = ws_layout(Bc, ga.T, ga.C, ga.G);
+  const GnPlan p = sums_plan(Bc, ga.T, ga.C, dt);
+  char* base = static_cast<char*>(ws);
+  ga.x = static_cast<const char*>(ga.x) + static_cast<size_t>(b0) * ga.T * ga.C * dp::dtype_size(dt);
+  ga.b0 = b0;
+  ga.counters = reinterpret_cast<unsigned*>(base);
+  ga.counter_stride = w.counter_stride;
+  ga.sums = reinterpret_cast<float*>(base + w.sums_off);
+  ga.coef = table ? reinterpret_cast<float*>(base + w.coef_off) : nullptr;
+  ga.partial = reinterpret_cast<float2*>(base + w.partial_off);
+  ga.fresh = fresh;
+  ga.tiles = p.tiles;
+  ga.tile_tokens = p.tile_tokens;
+  const dim3 grid(static_cast<unsigned>(p.tiles), static_cast<unsigned>(Bc));
+  if (dt == DP_BF16) hipLaunchKernelGGL(gn_partial<true>, grid, dim3(kThreads), 0, st, ga);
+  else hipLaunchKernelGGL(gn_partial<false>, grid, dim3(kThreads), 0, st, ga);
+}
+
+// Apply pass over batch items [b0, b0 + Bc): from the coefficient table
+// `coef` ([Bc][2][C], written by the sums pass) when given, else from the
+// local sums `local_sums` ([Bc][G][2]) and the stale sums.
+void launch_apply(GnArgs ga, int b0, int Bc, const float* local_sums, float* coef, void* y, dp_dtype dt,
+                  hipStream_t st) {
+  const GnPlan p = apply_plan(ga.T, ga.C, dt);
+  const size_t off = static_cast<size_t>(b0) * ga.T * ga.C * dp::dtype_size(dt);
+  ga.x = static_cast<const char*>(ga.x) + off;
+  ga.y = static_cast<char*>(y) + off;
+  ga.b0 = b0;
+  ga.given = local_sums;
+  ga.coef = coef;
+  ga.tiles = p.tiles;
+  ga.tile_tokens = p.tile_tokens;
+  const dim3 grid(static_cast<unsigned>(p.tiles), static_cast<unsigned>(Bc));
+  const bool wide = apply_threads(ga.C, dt) == 512;
+  const int k = (coef ? 8 : 0) + (dt == DP_BF16 ? 4 : 0) + (wide ? 2 : 0) + (ga.silu ? 1 : 0);
+  switch (k) {
+#define DP_GN_APPLY(K, KERN, BF, NT, SI) \
+  case K: hipLaunchKernelGGL((KERN<BF, NT, SI>), grid, dim3(NT), 0, st, ga); break;
+    DP_GN_APPLY(0, gn_apply_sums, false, 256, false)
+    DP_GN_APPLY(1, gn_apply_sums, false, 256, true)
+    DP_GN_APPLY(2, gn_apply_sums, false, 512, false)
+    DP_GN_APPLY(3, gn_apply_sums, false, 512, true)
+    DP_GN_APPLY(4, gn_apply_sums, true, 256, false)
+    DP_GN_APPLY(5, gn_apply_sums, true, 256, true)
+    DP_GN_APPLY(6, gn_apply_sums, true, 512, false)
+    DP_GN_APPLY(7, gn_apply_sums, true, 512, true)
+    DP_GN_APPLY(8, gn_apply_table, false, 256, false)
+    DP_GN_APPLY(9, gn_apply_table, false, 256, true)
+    DP_GN_APPLY(10, gn_apply_table, false, 512, false)
+    DP_GN_APPLY(11, gn_apply_table, false, 512, true)
+    DP_GN_APPLY(12, gn_apply_table, true, 256, false)
+    DP_GN_APPLY(13, gn_apply_table, true, 256, true)
+    DP_GN_APPLY(14, gn_apply_table, true, 512, false)
+    DP_GN_APPLY(15, gn_apply_table, true, 512, true)
+#undef DP_GN_APPLY
+  }
 }
 
 }  // namespace
 
 DP_API size_t dp_groupnorm_stale_stats_workspace(int64_t B, int64_t T_loc, int64_t C, int64_t G) {
-  (void)C;
-  if (B <= 0 || T_loc <= 0 || G <= 0) return 0;
-  return workspace_bytes(B, T_loc, G);
+  if (B <= 0 || T_loc <= 0 || C <= 0 || G <= 0) return 0;
+  return ws_bytes(B, T_loc, C, G);
 }
 
 DP_API dp_status dp_groupnorm_stale_stats(const void* x, const float* stale_sums, int64_t n_patches,
@@ -453,100 +761,47 @@ DP_API dp_status dp_groupnorm_stale_stats(const void* x, const float* stale_sums
                                           const float* beta, float eps, int fuse_silu, void* y,
                                           float* fresh_sums_out, int64_t B, int64_t T_loc,
                                           int64_t C, int64_t G, dp_dtype dt, void* ws,
-                                          size_t ws_bytes, hipStream_t stream) {
+                                          size_t ws_size, hipStream_t stream) {
   using dp::fail;
-  if (!x || !y) return fail(DP_ERR_INVALID_ARG, "dp_groupnorm_stale_stats: NULL x or y");
-  if (B <= 0 || T_loc <= 0 || C <= 0 || G <= 0 || n_patches <= 0)
-    return fail(DP_ERR_INVALID_ARG, "dp_groupnorm_stale_stats: sizes must be positive");
-  if (!stale_sums && n_patches > 1)
-    return fail(DP_ERR_INVALID_ARG, "dp_groupnorm_stale_stats: NULL stale_sums with %lld patches",
-                (long long)n_patches);
-  if (rank < 0 || rank >= n_patches)
-    return fail(DP_ERR_INVALID_ARG, "dp_groupnorm_stale_stats: rank %lld outside [0, %lld)",
-                (long long)rank, (long long)n_patches);
-  if (T_total < T_loc)
-    return fail(DP_ERR_INVALID_ARG, "dp_groupnorm_stale_stats: T_total < T_loc");
-  if (!(eps >= 0.f)) return fail(DP_ERR_INVALID_ARG, "dp_groupnorm_stale_stats: eps must be >= 0");
-  if (C % G != 0) return fail(DP_ERR_INVALID_ARG, "dp_groupnorm_stale_stats: C %% G != 0");
-  if (!dp::dtype_ok(dt)) return fail(DP_ERR_INVALID_ARG, "dp_groupnorm_stale_stats: bad dtype");
-  const size_t need = workspace_bytes(B, T_loc, G);
-  if (!ws || ws_bytes < need)
-    return fail(DP_ERR_INVALID_ARG, "dp_groupnorm_stale_stats: workspace %zu < %zu bytes",
-                ws_bytes, need);
-  const int vec = dt == DP_BF16 ? 8 : 4;
-  if (C % vec != 0 || C > 2048 || C / vec > kThreads || T_loc > 0x7FFFFFFF || B > 65535 ||
-      B * G > 0x7FFFFFFF)
-    return fail(DP_ERR_UNSUPPORTED, "dp_groupnorm_stale_stats: C=%lld G=%lld not supported",
-                (long long)C, (long long)G);
-  const size_t es = dp::dtype_size(dt);
-  const size_t xb = static_cast<size_t>(B * T_loc * C) * es;
-  if (dp::overlaps(x, xb, y, xb)) return fail(DP_ERR_INVALID_ARG, "dp_groupnorm_stale_stats: x and y overlap");
-
-  const GnPlan p = make_plan(B, T_loc, C, dt);
+  const char* name = "dp_groupnorm_stale_stats";
+  if (!x || !y) return fail(DP_ERR_INVALID_ARG, "%s: NULL x or y", name);
   GnArgs ga{};
-  ga.x = x;
-  ga.y = y;
-  ga.partial = static_cast<float2*>(ws);
-  ga.stale = stale_sums;
-  ga.gamma = gamma;
-  ga.beta = beta;
-  ga.fresh = fresh_sums_out;
-  ga.T = static_cast<int>(T_loc);
-  ga.C = static_cast<int>(C);
-  ga.G = static_cast<int>(G);
-  ga.tiles = p.tiles;
-  ga.tile_tokens = p.tile_tokens;
-  ga.n_patches = static_cast<int>(n_patches);
-  ga.rank = static_cast<int>(rank);
-  ga.B = static_cast<int>(B);
-  ga.silu = fuse_silu;
-  ga.inv_count = static_cast<float>(1.0 / (static_cast<double>(T_total) * (C / G)));
-  ga.eps = eps;
-  const dim3 grid(static_cast<unsigned>(p.tiles), static_cast<unsigned>(B));
+  dp_status st = check_common(name, x, B, T_loc, C, G, dt, ga);
+  if (st != DP_OK) return st;
+  if ((st = check_stats_args(name, stale_sums, n_patches, rank, T_total, T_loc, eps)) != DP_OK) return st;
+  const size_t need = ws_bytes(B, T_loc, C, G);
+  if (!ws || ws_size < need) return fail(DP_ERR_INVALID_ARG, "%s: workspace %zu < %zu bytes", name, ws_size, need);
+  const size_t xb = static_cast<size_t>(B * T_loc * C) * dp::dtype_size(dt);
+  if (dp::overlaps(x, xb, y, xb)) return fail(DP_ERR_INVALID_ARG, "%s: x and y overlap", name);
+  set_stats(ga, stale_sums, n_patches, rank, T_total, gamma, beta, eps, fuse_silu);
   dp::clear_error();
-  if (dt == DP_BF16) {
-    hipLaunchKernelGGL(gn_partial<true>, grid, dim3(kThreads), 0, stream, ga);
-    hipLaunchKernelGGL(gn_apply<true>, grid, dim3(kThreads), 0, stream, ga);
-  } else {
-    hipLaunchKernelGGL(gn_partial<false>, grid, dim3(kThreads), 0, stream, ga);
-    hipLaunchKernelGGL(gn_apply<false>, grid, dim3(kThreads), 0, stream, ga);
+  for (int64_t b0 = 0; b0 < B; b0 += kMaxChunk) {
+    const int Bc = static_cast<int>(std::min<int64_t>(kMaxChunk, B - b0));
+    launch_sums(ga, static_cast<int>(b0), Bc, ws, fresh_sums_out ? fresh_sums_out + b0 * G * 2 : nullptr, true, dt,
+                stream);
+    launch_apply(ga, static_cast<int>(b0), Bc, nullptr,
+                 reinterpret_cast<float*>(static_cast<char*>(ws) + ws_layout(Bc, T_loc, C, G).coef_off), y, dt, stream);
   }
-  return dp::check_launch("dp_groupnorm_stale_stats");
+  return dp::check_launch(name);
 }
 
 DP_API dp_status dp_groupnorm_sums(const void* x, float* sums_out, int64_t B, int64_t T_loc, int64_t C, int64_t G,
-                                   dp_dtype dt, void* ws, size_t ws_bytes, hipStream_t stream) {
+                                   dp_dtype dt, void* ws, size_t ws_size, hipStream_t stream) {
   using dp::fail;
   const char* name = "dp_groupnorm_sums";
   if (!x || !sums_out) return fail(DP_ERR_INVALID_ARG, "%s: NULL x or sums_out", name);
-  if (B <= 0 || T_loc <= 0 || C <= 0 || G <= 0) return fail(DP_ERR_INVALID_ARG, "%s: sizes must be positive", name);
-  if (C % G != 0) return fail(DP_ERR_INVALID_ARG, "%s: C %% G != 0", name);
-  if (!dp::dtype_ok(dt)) return fail(DP_ERR_INVALID_ARG, "%s: bad dtype", name);
-  const size_t need = workspace_bytes(B, T_loc, G);
-  if (!ws || ws_bytes < need) return fail(DP_ERR_INVALID_ARG, "%s: workspace %zu < %zu bytes", name, ws_bytes, need);
-  const int vec = dt == DP_BF16 ? 8 : 4;
-  if (C % vec != 0 || C > 2048 || C / vec > kThreads || T_loc > 0x7FFFFFFF || B > 65535 || B * G > 0x7FFFFFFF)
-    return fail(DP_ERR_UNSUPPORTED, "%s: C=%lld G=%lld not supported", name, (long long)C, (long long)G);
+  GnArgs ga{};
+  dp_status st = check_common(name, x, B, T_loc, C, G, dt, ga);
+  if (st != DP_OK) return st;
+  const size_t need = ws_bytes(B, T_loc, C, G);
+  if (!ws || ws_size < need) return fail(DP_ERR_INVALID_ARG, "%s: workspace %zu < %zu bytes", name, ws_size, need);
   const size_t xb = static_cast<size_t>(B * T_loc * C) * dp::dtype_size(dt);
   if (dp::overlaps(x, xb, sums_out, static_cast<size_t>(B * G) * 8) || dp::overlaps(ws, need, sums_out, static_cast<size_t>(B * G) * 8))
     return fail(DP_ERR_INVALID_ARG, "%s: sums_out overlaps x or the workspace", name);
-  const GnPlan p = make_plan(B, T_loc, C, dt);
-  GnArgs ga{};
-  ga.x = x;
-  ga.partial = static_cast<float2*>(ws);
-  ga.fresh = sums_out;
-  ga.T = static_cast<int>(T_loc);
-  ga.C = static_cast<int>(C);
-  ga.G = static_cast<int>(G);
-  ga.tiles = p.tiles;
-  ga.tile_tokens = p.tile_tokens;
-  ga.n_patches = 1;
-  ga.B = static_cast<int>(B);
   dp::clear_error();
-  const dim3 grid(static_cast<unsigned>(p.tiles), static_cast<unsigned>(B));
-  if (dt == DP_BF16) hipLaunchKernelGGL(gn_partial<true>, grid, dim3(kThreads), 0, stream, ga);
-  else hipLaunchKernelGGL(gn_partial<false>, grid, dim3(kThreads), 0, stream, ga);
-  hipLaunchKernelGGL(gn_sums, dim3(1, static_cast<unsigned>(B)), dim3(kThreads), 0, stream, ga);
+  for (int64_t b0 = 0; b0 < B; b0 += kMaxChunk)
+    launch_sums(ga, static_cast<int>(b0), static_cast<int>(std::min<int64_t>(kMaxChunk, B - b0)), ws,
+                sums_out + b0 * G * 2, false, dt, stream);
   return dp::check_launch(name);
 }
 
@@ -557,40 +812,14 @@ DP_API dp_status dp_groupnorm_apply(const void* x, const float* local_sums, cons
   using dp::fail;
   const char* name = "dp_groupnorm_apply";
   if (!x || !y || !local_sums) return fail(DP_ERR_INVALID_ARG, "%s: NULL x, y or local_sums", name);
-  if (B <= 0 || T_loc <= 0 || C <= 0 || G <= 0 || n_patches <= 0) return fail(DP_ERR_INVALID_ARG, "%s: sizes must be positive", name);
-  if (!stale_sums && n_patches > 1) return fail(DP_ERR_INVALID_ARG, "%s: NULL stale_sums with %lld patches", name, (long long)n_patches);
-  if (rank < 0 || rank >= n_patches) return fail(DP_ERR_INVALID_ARG, "%s: rank outside [0, n_patches)", name);
-  if (T_total < T_loc) return fail(DP_ERR_INVALID_ARG, "%s: T_total < T_loc", name);
-  if (!(eps >= 0.f)) return fail(DP_ERR_INVALID_ARG, "%s: eps must be >= 0", name);
-  if (C % G != 0) return fail(DP_ERR_INVALID_ARG, "%s: C %% G != 0", name);
-  if (!dp::dtype_ok(dt)) return fail(DP_ERR_INVALID_ARG, "%s: bad dtype", name);
-  const int vec = dt == DP_BF16 ? 8 : 4;
-  if (C % vec != 0 || C > 2048 || C / vec > kThreads || T_loc > 0x7FFFFFFF || B > 65535 || B * G > 0x7FFFFFFF)
-    return fail(DP_ERR_UNSUPPORTED, "%s: C=%lld G=%lld not supported", name, (long long)C, (long long)G);
+  GnArgs ga{};
+  dp_status st = check_common(name, x, B, T_loc, C, G, dt, ga);
+  if (st != DP_OK) return st;
+  if ((st = check_stats_args(name, stale_sums, n_patches, rank, T_total, T_loc, eps)) != DP_OK) return st;
   const size_t xb = static_cast<size_t>(B * T_loc * C) * dp::dtype_size(dt);
   if (dp::overlaps(x, xb, y, xb)) return fail(DP_ERR_INVALID_ARG, "%s: x and y overlap", name);
-  const GnPlan p = make_plan(B, T_loc, C, dt);
-  GnArgs ga{};
-  ga.x = x;
-  ga.y = y;
-  ga.given = local_sums;
-  ga.stale = stale_sums;
-  ga.gamma = gamma;
-  ga.beta = beta;
-  ga.T = static_cast<int>(T_loc);
-  ga.C = static_cast<int>(C);
-  ga.G = static_cast<int>(G);
-  ga.tiles = p.tiles;
-  ga.tile_tokens = p.tile_tokens;
-  ga.n_patches = static_cast<int>(n_patches);
-  ga.rank = static_cast<int>(rank);
-  ga.B = static_cast<int>(B);
-  ga.silu = fuse_silu;
-  ga.inv_count = static_cast<float>(1.0 / (static_cast<double>(T_total) * (C / G)));
-  ga.eps = eps;
+  set_stats(ga, stale_sums, n_patches, rank, T_total, gamma, beta, eps, fuse_silu);
   dp::clear_error();
-  const dim3 grid(static_cast<unsigned>(p.tiles), static_cast<unsigned>(B));
-  if (dt == DP_BF16) hipLaunchKernelGGL(gn_apply<true>, grid, dim3(kThreads), 0, stream, ga);
-  else hipLaunchKernelGGL(gn_apply<false>, grid, dim3(kThreads), 0, stream, ga);
+  launch_apply(ga, 0, static_cast<int>(B), local_sums, nullptr, y, dt, stream);
   return dp::check_launch(name);
 }

@@ -41,7 +41,9 @@ def _stream() -> int:
 
 
 def _ws(nbytes: int, device) -> torch.Tensor | None:
-    return torch.empty(nbytes, dtype=torch.uint8, device=device) if nbytes else None
+    # zero-filled: the GroupNorm and conv-sums workspaces hold ticket counters
+    # that must start at zero (every call leaves them at zero again)
+    return torch.zeros(nbytes, dtype=torch.uint8, device=device) if nbytes else None
 
 
 def dp_kv_buffer_splice(k_buf, v_buf, k_fresh, v_fresh, t0: int) -> None:

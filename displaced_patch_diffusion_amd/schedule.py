@@ -67,7 +67,7 @@ class DisplacedSchedule:
         Tq_max = heights[-1] * W
         attn_bytes = max(ops.dp_attn_stale_kv_workspace(B, heads, h * W, T, C // heads, dt) for h in heights)
         self.attn_ws = torch.empty(max(1, attn_bytes), dtype=torch.uint8, device=dev)
-        self.gn_ws = torch.empty(ops.dp_groupnorm_stale_stats_workspace(B, Tq_max, C, G),
+        self.gn_ws = torch.zeros(ops.dp_groupnorm_stale_stats_workspace(B, Tq_max, C, G),
                                  dtype=torch.uint8, device=dev)
         self.cur = 0
         self.has_prev = False

@@ -259,8 +259,7 @@ def test_share_end_to_end(name):
     query rows feeding sampled conv pixels, and the GroupNorm statistics of the
     whole band (which would need the band's full attention, 2.1 TFLOP in
     float64) are the oracle's sums of the device's conv output.  The errors are
-    printed; the bound is the per-stage bf16 tolerance widened for the chained
-    bf16 storage points."""
+    printed and held to the bf16 tolerance."""
     w = synth.WORKLOADS[name]
     say("chain end to end", name)
     st = drawn_state(w)
@@ -332,6 +331,7 @@ def test_share_end_to_end(name):
         assert v <= E2E_ATOL, f"{name} end to end, {k}: {v:.3e} > {E2E_ATOL}"
 
 
-# bf16 storage points between the chain's stages each add up to half an ulp of
-# the stored value; the end-to-end bound allows twice the per-stage tolerance.
-E2E_ATOL = 2 * BF16_ATOL
+# The bf16 tolerance holds end to end as well (largest errors measured on
+# MI355X: 1.4e-2 and 1.5e-2 at the two SDXL-1024^2 shares, from q stored in
+# bf16 with |q| in [4, 8) and the GroupNorm output's own rounding).
+E2E_ATOL = BF16_ATOL

@@ -2,8 +2,10 @@
 
 dp_conv3x3_stale_halo_gn_sums must write exactly dp_conv3x3_stale_halo's y
 and sums equal to the oracle's group sums of that y (float32 accumulation:
-within 2e-5 of sum|y| and of sum y^2); dp_groupnorm_apply with the sums
-dp_groupnorm_sums returns must equal dp_groupnorm_stale_stats bit for bit.
+within 2e-5 of sum|y| and of sum y^2), whether the last tile of each batch
+item folds them or a fold launch does; dp_groupnorm_apply with the sums
+dp_groupnorm_sums returns must equal dp_groupnorm_stale_stats bit for bit;
+workspaces reused across calls and shapes keep working.
 """
 from __future__ import annotations
 
@@ -39,6 +41,7 @@ def check_sums(g, y, G):
     (3, 7, 50, 64, 64, 8, "bottom"),      # small: 64x64 tiles, three batch items
     (2, 64, 256, 320, 320, 32, "both"),   # the SDXL-2048 conv (128x160 tiles)
     (1, 40, 300, 96, 128, 16, "none"),    # Cin % 64 != 0: 32-wide slices
+    (1, 256, 1024, 128, 128, 32, "both"), # a VAE band: too many partials for one block, the fold is its own launch
 ])
 def test_conv_gn_sums(B, h, W, Cin, Cout, G, halos):
     say("conv+gn sums", B, h, W, Cin, Cout, G, halos)
@@ -69,3 +72,39 @@ def test_groupnorm_apply_equals_stale_stats(dt, B, T, C, G, N, silu):
     y2 = ops.dp_groupnorm_stale_stats(x, st, 1, N * T, gm, bt, 1e-5, silu, G)
     torch.cuda.synchronize()
     assert torch.equal(y1, y2)
+
+
+def test_workspaces_reused_across_calls_and_shapes():
+    """One workspace per call kind, used by a run of calls whose tile counts
+    and batch sizes change from call to call: the ticket counters must come
+    back to zero after every call, so each call folds its own sums exactly
+    once (sums against the oracle each time, outputs identical to a call on a
+    fresh zero-filled workspace)."""
+    gn_shapes = [(2, 7200, 640, 32), (1, 17, 64, 8), (3, 5000, 128, 32), (2, 40000, 320, 32), (1, 1, 64, 32),
+                 (2, 7200, 640, 32)]
+    need = max(ops.dp_groupnorm_stale_stats_workspace(B, T, C, G) for B, T, C, G in gn_shapes)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    for i, (B, T, C, G) in enumerate(gn_shapes * 2):
+        say("gn workspace reuse", i, B, T, C, G)
+        x = R(40 + i, "wsr.x", (B, T, C), "bf16", 1.3)
+        gx = dev(x, "bf16")
+        s = ops.dp_groupnorm_sums(gx, G, ws=ws)
+        fresh = torch.empty_like(s)
+        y = ops.dp_groupnorm_stale_stats(gx, None, 0, T, None, None, 1e-5, i % 2 == 1, G, fresh_sums_out=fresh, ws=ws)
+        y_ref = ops.dp_groupnorm_stale_stats(gx, None, 0, T, None, None, 1e-5, i % 2 == 1, G)
+        torch.cuda.synchronize()
+        check_sums(host(s), x, G)
+        assert torch.equal(fresh, s) and torch.equal(y, y_ref)
+    conv_shapes = [(2, 30, 240, 640, 640, 32), (3, 7, 50, 64, 64, 8), (2, 13, 100, 64, 160, 32), (1, 40, 300, 96, 128, 16),
+                   (1, 256, 1024, 128, 128, 32)]
+    need = max(ops.dp_conv3x3_gn_sums_workspace(B, h, W, Co) for B, h, W, Ci, Co, G in conv_shapes)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    for i, (B, h, W, Cin, Cout, G) in enumerate(conv_shapes * 2):
+        say("conv sums workspace reuse", i, B, h, W, Cin, Cout, G)
+        x = dev(R(60 + i, "wsr.cx", (B, h, W, Cin), "bf16"), "bf16")
+        w = dev(R(0, "wsr.cw", (Cout, 3, 3, Cin), "bf16", (9 * Cin) ** -0.5), "bf16")
+        y, sums = ops.dp_conv3x3_stale_halo_gn_sums(x, None, None, w, None, G, ws=ws)
+        torch.cuda.synchronize()
+        check_sums(host(sums), host(y).reshape(B, h * W, Cout), G)
+    # the first batch item's top counter is back at zero
+    assert int(ws[:4].view(torch.int32)[0]) == 0
