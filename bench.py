@@ -25,7 +25,6 @@ event between ops adds queue time.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import platform
@@ -282,7 +281,7 @@ class Share:
 
 
 DEFAULT_QKV = "fused"
-DEFAULT_GN_SUMS = "separate"
+DEFAULT_GN_SUMS = "conv"
 
 
 def make_share(w, qkv: str = DEFAULT_QKV, gn_sums: str = DEFAULT_GN_SUMS):
@@ -393,9 +392,9 @@ def vae_rows_timing(torch, ops, synth, name: str, steps: int):
     def layer_ops(i, xin):
         sums, top, bot = layer[i]
         return [("sums", lambda: ops.dp_groupnorm_sums(xin.view(B, T, v.C), v.G, out=own, ws=ws)),
-                ("gn", lambda: ops.dp_groupnorm_stale_stats(xin.view(B, T, v.C), sums, r, v.H * v.W,
-                                                            wts[f"gamma{i}"], wts[f"beta{i}"], v.eps, True, v.G,
-                                                            y=y.view(B, T, v.C), ws=ws)),
+                ("gn", lambda: ops.dp_groupnorm_apply(xin.view(B, T, v.C), own, sums, r, v.H * v.W,
+                                                      wts[f"gamma{i}"], wts[f"beta{i}"], v.eps, True, v.G,
+                                                      y=y.view(B, T, v.C))),
                 ("conv", lambda: ops.dp_conv3x3_stale_halo(y, top, bot, wts[f"w{i}"], wts[f"b{i}"], y=z[i]))]
 
     band_ops = layer_ops(0, x0) + layer_ops(1, z[0])
@@ -498,23 +497,198 @@ def _cpu_model():
 
 # ----------------------------------------------------------- counter traffic
 def _traffic_from_profile(w):
-    """HBM bytes per attention launch from the committed rocprofv3 counter
-    summary, if it was taken on the current attention source."""
-    path = os.path.join(ROOT, "profiles", f"attn_{w.name}_counters.txt")
-    src = os.path.join(ROOT, "displaced_patch_diffusion_amd", "csrc", "attention.hip")
+    """L2<->fabric bytes per call of the attention op (its kernels summed)
+    from the committed rocprofv3 counter summary of this workload, if that
+    summary was taken on the current attention source."""
+    from displaced_patch_diffusion_amd import build, rocprof_summary
+
+    rec = rocprof_summary.read_result(os.path.join(ROOT, "profiles", f"counters_{w.name}.txt"))
+    if not rec:
+        return None
+    now = build.source_digest()
+    if any(rec.get("sources_sha256", {}).get(f) != now.get(f) for f in ("attention.hip", "dp_internal.h")):
+        return None
+    a = rec.get("ops", {}).get("attn", {})
+    if "read_bytes" not in a or "write_bytes" not in a:
+        return None
+    return int(a["read_bytes"] + a["write_bytes"])
+
+
+# ------------------------------------------------------------------ timing
+class Flusher:
+    """A 1 GiB buffer written before every cold repetition, outside its event
+    pair: larger than the eight 4 MB L2s and the 256 MB last-level cache, so a
+    cold repetition reads its inputs from HBM."""
+
+    BYTES = 1 << 30
+
+    def __init__(self, torch):
+        self.buf = torch.empty(self.BYTES, dtype=torch.uint8, device="cuda")
+
+    def __call__(self):
+        self.buf.zero_()
+
+
+def event_medians_us(torch, fn, reps: int, flush=None) -> float:
+    """Median over `reps` repetitions of [flush;] event; fn(); event, in us.
+    All pairs are recorded on torch's current stream, where every library
+    call launches, and read after one synchronisation."""
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    fn()
+    torch.cuda.synchronize()
+    for e0, e1 in evs:
+        if flush is not None:
+            flush()
+        e0.record()
+        fn()
+        e1.record()
+    torch.cuda.synchronize()
+    return float(np.median([e0.elapsed_time(e1) * 1e3 for e0, e1 in evs]))
+
+
+def measure_ops(torch, share, K: int, reps: int, flush):
+    """Per op of the step (ops of one name summed): the back-to-back average
+    of K launches (hot; the per-op figure the fractions use), and the hot and
+    cold (flushed) medians of single launches between an event pair (these
+    include an event pair's few microseconds of queue time)."""
+    b2b, hot, cold = {}, {}, {}
+    for name, fn in share.ops_:
+        b2b[name] = b2b.get(name, 0.0) + back_to_back_us(torch, fn, K)
+        hot[name] = hot.get(name, 0.0) + event_medians_us(torch, fn, reps)
+        cold[name] = cold.get(name, 0.0) + event_medians_us(torch, fn, reps, flush)
+    return b2b, hot, cold
+
+
+def kernel_table(w, b2b, hot, cold):
+    fl, by = w.flops(), w.bytes()
+    peak_mfma = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
+    kern = {}
+    for name, t in b2b.items():
+        rec = {"us": round(t, 2), "us_hot_median": round(hot[name], 2), "us_cold_median": round(cold[name], 2)}
+        if name in fl:
+            a = fl[name] / t / 1e6
+            rec.update({"TFLOP/s": round(a, 1), "frac": round(a / peak_mfma, 4),
+                        "frac_cold": round(fl[name] / cold[name] / 1e6 / peak_mfma, 4)})
+        elif name in by:
+            a = by[name] / t / 1e3
+            rec.update({"GB/s": round(a, 1), "frac": round(a / PEAK_HBM_GBPS, 4),
+                        "frac_cold": round(by[name] / cold[name] / 1e3 / PEAK_HBM_GBPS, 4)})
+        kern[name] = rec
+    return kern
+
+
+def splice_timing(torch, ops, share, K: int, reps: int, flush):
+    """The K/V buffer splice at the share's shape (the step itself writes K/V
+    straight from the projection): fresh rows into both full-image buffers."""
+    w = share.w
+    fn = lambda: ops.dp_kv_buffer_splice(share.k_buf, share.v_buf, share.kf, share.vf, share.t0)
+    t = back_to_back_us(torch, fn, K)
+    cold = event_medians_us(torch, fn, reps, flush)
+    by = w.bytes()["splice"]
+    return {"us": round(t, 2), "GB/s": round(by / t / 1e3, 1), "frac": round(by / t / 1e3 / PEAK_HBM_GBPS, 4),
+            "us_cold_median": round(cold, 2), "frac_cold": round(by / cold / 1e3 / PEAK_HBM_GBPS, 4),
+            "bytes": by}
+
+
+def config_summary(torch, ops, synth, name: str, K: int, reps: int, flush):
+    """Another workload's share: per-op numbers and the step's medians."""
+    w = synth.WORKLOADS[name]
+    share = make_share(w)
+    for _ in range(3):
+        share.step(lambda n: None)
+    torch.cuda.synchronize()
+    b2b, hot, cold = measure_ops(torch, share, K, reps, flush)
+    step = lambda: share.step(lambda n: None)
+    step_hot = event_medians_us(torch, step, reps)
+    step_cold = event_medians_us(torch, step, reps, flush)
+    fl = w.flops()
+    out = {"workload": w.name, "note": w.note, "dtype": w.dtype,
+           "step_us_hot_median": round(step_hot, 2), "step_us_cold_median": round(step_cold, 2),
+           "TFLOP/s_hot": round(sum(fl.values()) / step_hot / 1e6, 1),
+           "kernels": kernel_table(w, b2b, hot, cold)}
+    if w.dtype == "bf16":
+        out["splice"] = splice_timing(torch, ops, share, K, reps, flush)
+    del share
+    torch.cuda.empty_cache()
+    return out
+
+
+# ------------------------------------------------------------ profile runs
+def profile_ops(torch, ops, share, reps: int, flush=None):
+    """For rocprofv3 runs: each op of the step launched `reps` times in a row,
+    in step order, then the K/V splice on the share's buffers (a plain copy of
+    known size, the counters' calibration).  A `torch.cuda._sleep` spin kernel
+    precedes each op's run and follows the last one, so the dispatch records
+    split at the spins and every segment belongs to one op.  With `flush`,
+    every launch follows a cache flush (a torch fill kernel, which the
+    summariser drops).  Returns the segment labels, which the run prints for
+    the summariser."""
+    labels, fns, seen = [], [], {}
+    for name, fn in share.ops_:
+        k = seen.get(name, 0)
+        seen[name] = k + 1
+        if name == "proj":
+            lab = ("qkv_proj" if k == 0 else "out_proj")
+        else:
+            lab = f"{name}{k}" if name in ("conv", "groupnorm") else name
+        labels.append(lab)
+        fns.append(fn)
+    labels.append("splice_copy")
+    fns.append(lambda: ops.dp_kv_buffer_splice(share.k_buf, share.v_buf, share.kf, share.vf, share.t0))
+    torch.cuda.synchronize()
+    for fn in fns:
+        torch.cuda._sleep(1000)
+        for _ in range(reps):
+            if flush is not None:
+                flush()
+            fn()
+        torch.cuda.synchronize()
+    torch.cuda._sleep(1000)
+    torch.cuda.synchronize()
+    return labels
+
+
+# ---------------------------------------------------------------- provenance
+def provenance(torch):
+    """Where the numbers come from: build revision and source digests,
+    ROCm/HIP/torch versions, device and its clocks as the SMI tools report
+    them after the timed work, host CPU."""
+    import subprocess
+
+    from displaced_patch_diffusion_amd import build as b
+
+    out = {}
     try:
-        with open(path) as f:
-            rec = None
-            for line in f:
-                if line.startswith("RESULT "):
-                    rec = json.loads(line[len("RESULT "):])
-        with open(src, "rb") as f:
-            sha = hashlib.sha256(f.read()).hexdigest()
+        with open(b.BUILD_INFO) as f:
+            info = json.load(f)
+        out["build_git_rev"] = info.get("git_rev")
+        out["hipcc"] = info.get("hipcc")
+        out["sources_match_build"] = info.get("sources_sha256") == b.source_digest()
     except (OSError, ValueError):
-        return None
-    if not rec or rec.get("attention_hip_sha256") != sha:
-        return None
-    return rec.get("traffic_bytes_per_launch")
+        out["build_git_rev"] = None
+    out["sources_sha256_16"] = {k: v[:16] for k, v in b.source_digest().items()}
+    try:
+        with open("/opt/rocm/.info/version") as f:
+            out["rocm_version"] = f.read().strip()
+    except OSError:
+        out["rocm_version"] = None
+    out["torch"] = torch.__version__
+    out["torch_hip"] = getattr(torch.version, "hip", None)
+    props = torch.cuda.get_device_properties(0)
+    out["device"] = {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
+                     "compute_units": props.multi_processor_count, "hbm_GiB": round(props.total_memory / 2 ** 30, 1)}
+    clocks = None
+    for cmd in (["rocm-smi", "--showclocks", "--json"], ["amd-smi", "metric", "--clock", "--json"]):
+        try:
+            r = subprocess.run(cmd, capture_output=True, text=True, timeout=20)
+            if r.returncode == 0 and r.stdout.strip():
+                clocks = {"tool": cmd[0], "report": json.loads(r.stdout)}
+                break
+        except (OSError, subprocess.SubprocessError, ValueError):
+            continue
+    out["clocks_after_timing"] = clocks
+    out["host"] = {"cpu_model": _cpu_model(), "cpus": os.cpu_count()}
+    return out
 
 
 # ---------------------------------------------------------------------- main
@@ -523,6 +697,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--reps", type=int, default=50, help="repetitions behind every hot and cold median")
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle's attention sample")
@@ -532,6 +707,12 @@ def main():
                          "pass; separate: the GroupNorm forms them in a read pass of its own")
     ap.add_argument("--no-otil", action="store_true", help="skip the OTIL selective-transmit timing")
     ap.add_argument("--no-vae", action="store_true", help="skip the row-sharded VAE decoder timing")
+    ap.add_argument("--no-configs", action="store_true", help="skip the other bf16 workloads' numbers")
+    ap.add_argument("--profile-ops", type=int, default=0, metavar="R",
+                    help="rocprofv3 mode: launch each op of the step R times in step order, spin kernels "
+                         "between the ops, print the op labels and exit (no timing)")
+    ap.add_argument("--profile-flush", action="store_true",
+                    help="with --profile-ops: flush the caches (1 GiB write) before every launch")
     ap.add_argument("--qkv", choices=("fused", "separate"), default=DEFAULT_QKV,
                     help="fused: one launch projects Q/K/V and writes K/V into the buffers; "
                          "separate: three projections then the K/V splice")
@@ -553,7 +734,6 @@ def main():
     torch.cuda.set_device(0)
     log(f"bench: workload {w.name}: building inputs")
     share = make_share(w, args.qkv, args.gn_sums)
-
     names = []
 
     def collect(name):
@@ -564,23 +744,21 @@ def main():
         share.step(lambda n: None)
     torch.cuda.synchronize()
 
-    K = args.steps
-    # Per-op breakdown, before the timed steps: each op of the step enqueued K
-    # times back to back between two events, behind a GPU spin that lets the
-    # host queue them all, so neither event queue time nor host launch time
-    # enters the average.
-    per_op = {}
-    for name, fn in share.ops_:
-        fn()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda._sleep(2_000_000)
-        e0.record()
-        for _ in range(K):
-            fn()
-        e1.record()
-        torch.cuda.synchronize()
-        per_op[name] = per_op.get(name, 0.0) + e0.elapsed_time(e1) * 1e-3 / K
+    if args.profile_ops:
+        labels = profile_ops(torch, ops, share, args.profile_ops, Flusher(torch) if args.profile_flush else None)
+        print("PROFILE_OPS " + json.dumps({"workload": w.name, "reps": args.profile_ops, "labels": labels,
+                                           "flush": bool(args.profile_flush),
+                                           "qkv": args.qkv, "gn_sums": args.gn_sums,
+                                           "splice_bytes": w.bytes()["splice"]}), flush=True)
+        return
+    flush = Flusher(torch)
+    K, R = args.steps, args.reps
+    # Per-op breakdown, before the timed steps: the back-to-back average of K
+    # launches of each op (behind a GPU spin that lets the host queue them
+    # all, so neither event queue time nor host launch time enters it), and
+    # hot and cold medians of single launches.
+    log("bench: per-op timings")
+    b2b, hot, cold = measure_ops(torch, share, K, R, flush)
     # Timed region: K steps with HIP events only around the attention call (on
     # torch's current stream, where every library call launches); an event
     # between every op costs a few microseconds of queue time each.
@@ -605,29 +783,24 @@ def main():
     wall = time.perf_counter() - t0
     log(f"bench: {K} steps in {wall:.4f}s")
     attn_t = sum(a.elapsed_time(b) for a, b in att) * 1e-3 / K
+    # the whole step's medians, after the timed region
+    step = lambda: share.step(lambda n: None)
+    step_hot = event_medians_us(torch, step, R)
+    step_cold = event_medians_us(torch, step, R, flush)
 
-    per_op["attn"] = attn_t
-    fl, by = w.flops(), w.bytes()
+    fl = w.flops()
     step_s = wall / K
     work = sum(fl.values())
     value = work / step_s / 1e12
     peak_mfma = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
-    kern = {}
-    for name, t in per_op.items():
-        if name in fl:
-            a = fl[name] / t / 1e12
-            kern[name] = {"us": round(t * 1e6, 2), "TFLOP/s": round(a, 1), "frac": round(a / peak_mfma, 4)}
-        elif name in by:
-            a = by[name] / t / 1e9
-            kern[name] = {"us": round(t * 1e6, 2), "GB/s": round(a, 1), "frac": round(a / PEAK_HBM_GBPS, 4)}
+    b2b["attn"] = attn_t * 1e6  # the timed steps' own attention time
+    kern = kernel_table(w, b2b, hot, cold)
     achieved = fl["attn"] / attn_t / 1e12
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak_mfma,
                 "unit": "TFLOP/s", "frac": round(achieved / peak_mfma, 4),
                 "traffic": _traffic_from_profile(w), "kernel": "attn_bf16_d64",
                 "work_per_launch": f"{fl['attn'] / 1e9:.2f} GFLOP"}
-    props = torch.cuda.get_device_properties(0)
-    device = {"name": props.name, "arch": getattr(props, "gcnArchName", ""), "compute_units": props.multi_processor_count,
-              "hbm_GiB": round(props.total_memory / 2 ** 30, 1)}
+    splice = splice_timing(torch, ops, share, K, R, flush) if w.dtype == "bf16" else None
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": K, "warmup": args.warmup, "ms_per_step": round(step_s * 1e3, 4),
@@ -638,12 +811,25 @@ def main():
                    "conv_level": f"{w.conv_H}x{w.conv_W}", "C_conv": w.conv_C, "n_patches": w.N,
                    "rank": w.rank, "Tq": w.Tq, "T_kv": w.T_kv, "qkv": args.qkv, "gn_sums": args.gn_sums,
                    "parallelism": "one rank's share, 1 GPU"},
-        "device": device,
         "roofline": roofline,
         "kernels": kern,
         "groupnorm_GBps": kern.get("groupnorm", {}).get("GB/s"),
+        "splice": splice,
+        "step_us_hot_median": round(step_hot, 2), "step_us_cold_median": round(step_cold, 2),
+        "timing": {"reps": R, "flush_bytes": Flusher.BYTES,
+                   "per_op_us": "average of K back-to-back launches (hot)",
+                   "medians": "median of reps single launches between an event pair; cold reps flush "
+                              "the caches with a 1 GiB write outside the pair"},
         "flops_counted": {k2: v2 for k2, v2 in fl.items()},
     }
+    del share
+    torch.cuda.empty_cache()
+    if not args.no_configs:
+        others = [n for n in synth.WORKLOAD_ORDER if n != w.name and synth.WORKLOADS[n].dtype == "bf16"]
+        out["configs"] = {}
+        for n in others:
+            log(f"bench: workload {n}")
+            out["configs"][n] = config_summary(torch, ops, synth, n, 10, 20, flush)
     if not args.no_otil:
         out["otil"] = otil_timing(torch, ops, synth, 20)
     if not args.no_vae:
@@ -652,6 +838,7 @@ def main():
     if not args.no_cpu_baseline:
         log("bench: CPU baseline (oracle on a bounded sample)")
         out["cpu_baseline"] = cpu_baseline(w, synth, args.cpu_seconds)
+    out["provenance"] = provenance(torch)
     print(json.dumps(out), flush=True)
 
 

@@ -7,6 +7,8 @@ to this file so that it travels with the source tree.
 """
 from __future__ import annotations
 
+import hashlib
+import json
 import os
 import subprocess
 import sys
@@ -48,6 +50,37 @@ def _compile(src: str) -> str:
     return obj
 
 
+BUILD_INFO = os.path.join(PKG, "build_info.json")
+
+
+def source_digest() -> dict:
+    """SHA-256 of every library source and header (identifies what a built
+    library was compiled from; also recomputed by the benchmark)."""
+    out = {}
+    for name in sorted(os.listdir(CSRC)):
+        with open(os.path.join(CSRC, name), "rb") as f:
+            out[name] = hashlib.sha256(f.read()).hexdigest()
+    with open(os.path.join(INCLUDE, "dp.h"), "rb") as f:
+        out["dp.h"] = hashlib.sha256(f.read()).hexdigest()
+    return out
+
+
+def _git(*args) -> str | None:
+    try:
+        r = subprocess.run(["git", "-C", ROOT, *args], capture_output=True, text=True, timeout=10)
+        return r.stdout.strip() if r.returncode == 0 else None
+    except (OSError, subprocess.SubprocessError):
+        return None
+
+
+def _git_rev() -> str | None:
+    """HEAD's revision, suffixed "-dirty" when tracked files differ from it."""
+    rev = _git("rev-parse", "HEAD")
+    if rev and _git("status", "--porcelain", "--untracked-files=no"):
+        rev += "-dirty"
+    return rev
+
+
 def build(jobs: int = 8) -> str:
     os.makedirs(BUILD, exist_ok=True)
     with ThreadPoolExecutor(max_workers=jobs) as ex:
@@ -58,6 +91,10 @@ def build(jobs: int = 8) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
     os.replace(tmp, LIB)
+    ver = subprocess.run([HIPCC, "--version"], capture_output=True, text=True).stdout.strip().splitlines()
+    info = {"git_rev": _git_rev(), "arch": ARCH, "hipcc": ver[:2], "sources_sha256": source_digest()}
+    with open(BUILD_INFO, "w") as f:
+        json.dump(info, f, indent=1)
     return LIB
 
 

@@ -100,6 +100,21 @@ __device__ __forceinline__ float2 load_coherent(const float2* p) {
                                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
 }
 
+// Sum of v over `lanes` adjacent lanes (a power of two <= 64) by a fixed xor
+// butterfly: every lane ends with the same, order-fixed total.
+__device__ __forceinline__ float2 lane_sum(float2 v, int lanes) {
+  for (int off = 1; off < lanes; off <<= 1) {
+    v.x += __shfl_xor(v.x, off, 64);
+    v.y += __shfl_xor(v.y, off, 64);
+  }
+  return v;
+}
+// Largest power of two <= min(n, 64), at least 1.
+__device__ __forceinline__ int pow2_lanes(int n) {
+  n = n < 1 ? 1 : (n > 64 ? 64 : n);
+  return 1 << (31 - __clz(n));
+}
+
 // Tile rows [lo, hi] holding the output rows of batch item b.
 __device__ __forceinline__ int2 batch_tile_rows(int b, int gT, int BM) {
   return make_int2(static_cast<int>((static_cast<int64_t>(b) * gT) / BM),
@@ -472,9 +487,9 @@ __global__ void __launch_bounds__(64 * NW, OCC) gemm_bf16(GemmArgs g) {
             const bool on = m < g.M && m / g.gT - b0 == sg && nblk < g.N;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-              const float v = static_cast<float>(static_cast<__bf16>(acc[i][j][4 * q + e] + bq[q][e]));
-              s1[e] += on ? v : 0.f;
-              s2[e] += on ? v * v : 0.f;
+              const float y = static_cast<float>(static_cast<__bf16>(acc[i][j][4 * q + e] + bq[q][e]));
+              s1[e] += on ? y : 0.f;
+              s2[e] += on ? y * y : 0.f;
             }
           }
 #pragma unroll
@@ -495,18 +510,30 @@ __global__ void __launch_bounds__(64 * NW, OCC) gemm_bf16(GemmArgs g) {
     __syncthreads();
     const int n1 = min(n0 + BN, g.N);
     const int g_lo = n0 / g.Cg, nslots = (n1 - 1) / g.Cg - g_lo + 1;
-    for (int t = tid; t < nseg * nslots; t += 64 * NW) {
-      const int sg = t / nslots, jj = t - sg * nslots, gi = g_lo + jj;
-      const int c0 = max(gi * g.Cg, n0), c1 = min((gi + 1) * g.Cg, n1);
-      float2 acc2 = make_float2(0.f, 0.f);
-      for (int c = c0; c < c1; ++c)
+    {
+      // `sl` adjacent lanes per (segment, slot): lane l takes the slot's
+      // channels l, l + sl, ... (all WGM wave rows each), then a lane tree
+      const int sl = pow2_lanes((64 * NW) / (nseg * nslots));
+      for (int t = tid; t < ((nseg * nslots * sl + 63) / 64) * 64; t += 64 * NW) {
+        const int st = t / sl, l = t % sl;
+        float2 acc2 = make_float2(0.f, 0.f);
+        if (st < nseg * nslots) {
+          const int sg = st / nslots, jj = st - sg * nslots, gi = g_lo + jj;
+          const int c0 = max(gi * g.Cg, n0), c1 = min((gi + 1) * g.Cg, n1);
+          for (int c = c0 + l; c < c1; c += sl)
 #pragma unroll
-        for (int w = 0; w < WGM; ++w) {
-          const float2 v = chan[(sg * WGM + w) * BN + c - n0];
-          acc2.x += v.x;
-          acc2.y += v.y;
+            for (int w = 0; w < WGM; ++w) {
+              const float2 v = chan[(sg * WGM + w) * BN + c - n0];
+              acc2.x += v.x;
+              acc2.y += v.y;
+            }
         }
-      store_coherent(g.gpart + ((static_cast<int64_t>(tm) * 2 + sg) * g.tiles_n + tn) * g.slots + jj, acc2);
+        acc2 = lane_sum(acc2, sl);
+        if (st < nseg * nslots && l == 0) {
+          const int sg = st / nslots, jj = st - sg * nslots;
+          store_coherent(g.gpart + ((static_cast<int64_t>(tm) * 2 + sg) * g.tiles_n + tn) * g.slots + jj, acc2);
+        }
+      }
     }
     if (!g.ticket) return;
     // the block's partials are complete at the coherence point before its tickets
@@ -523,23 +550,48 @@ __global__ void __launch_bounds__(64 * NW, OCC) gemm_bf16(GemmArgs g) {
     const int mask = fold_mask;
     for (int sg = 0; sg < nseg; ++sg) {
       if (!(mask & (1 << sg))) continue;
-      // fold batch item b: lane q of each group takes its share of the
-      // group's (tile row, tile column) partials; the lanes are added in order
+      // Fold batch item b.  Its partials are one run of tiles_n * slots per
+      // tile row (the row's segment holding b): loaded all at once, coalesced,
+      // into LDS (the ring, free now); then lanes of each group add the
+      // group's slots from LDS, tile rows in order, then tile columns, and a
+      // lane tree combines them.
       const int b = b0 + sg;
-      const int lanes = g.G >= 64 * NW ? 1 : (64 * NW) / g.G;
-      float2* red = chan;  // [lanes][G], free again after the barrier above
+      const int2 r = batch_tile_rows(b, g.gT, BM);
+      const int run = g.tiles_n * g.slots, total = (r.y - r.x + 1) * run;
+      float2* part = reinterpret_cast<float2*>(lds);  // [rows][tiles_n][slots]
       __syncthreads();
-      for (int f = tid; f < lanes * g.G; f += 64 * NW)
-        red[f] = fold_group_lane<true>(g, b, f % g.G, f / g.G, lanes, BM, BN);
-      __syncthreads();
-      for (int gi = tid; gi < g.G; gi += 64 * NW) {
-        float2 sum = red[gi];
-        for (int q = 1; q < lanes; ++q) {
-          sum.x += red[q * g.G + gi].x;
-          sum.y += red[q * g.G + gi].y;
+      constexpr int U = 8;
+      for (int e0 = tid; e0 < total; e0 += U * 64 * NW) {
+        float2 v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int e = min(e0 + u * 64 * NW, total - 1), rr = e / run;
+          const int sgt = b - static_cast<int>((static_cast<int64_t>(r.x + rr) * BM) / g.gT);
+          v[u] = load_coherent(g.gpart + (static_cast<int64_t>(r.x + rr) * 2 + sgt) * run + (e - rr * run));
         }
-        g.gsums[(static_cast<int64_t>(b) * g.G + gi) * 2] = sum.x;
-        g.gsums[(static_cast<int64_t>(b) * g.G + gi) * 2 + 1] = sum.y;
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+          if (e0 + u * 64 * NW < total) part[e0 + u * 64 * NW] = v[u];
+      }
+      __syncthreads();
+      const int lanes = pow2_lanes((64 * NW) / g.G);
+      for (int f = tid; f < ((g.G * lanes + 63) / 64) * 64; f += 64 * NW) {
+        const int gi = f / lanes, q = f % lanes;
+        float2 sum = make_float2(0.f, 0.f);
+        if (gi < g.G) {
+          const int tn_lo = (gi * g.Cg) / BN, ntn = ((gi + 1) * g.Cg - 1) / BN - tn_lo + 1;
+          for (int rr = q; rr <= r.y - r.x; rr += lanes)
+            for (int c = 0; c < ntn; ++c) {
+              const float2 v = part[rr * run + (tn_lo + c) * g.slots + gi - ((tn_lo + c) * BN) / g.Cg];
+              sum.x += v.x;
+              sum.y += v.y;
+            }
+        }
+        sum = lane_sum(sum, lanes);
+        if (gi < g.G && q == 0) {
+          g.gsums[(static_cast<int64_t>(b) * g.G + gi) * 2] = sum.x;
+          g.gsums[(static_cast<int64_t>(b) * g.G + gi) * 2 + 1] = sum.y;
+        }
       }
     }
   }
@@ -626,8 +678,11 @@ void launch_bf16_gns(const GemmArgs& base, hipStream_t st) {
   const int64_t tiles_b = ((static_cast<int64_t>(g.gT) + t.bm - 1) / t.bm + 1) * g.tiles_n;
   const int64_t B = g.M / g.gT;
   g.counter_stride = static_cast<int>((1 + (tiles_b + kTicketGroup - 1) / kTicketGroup) * kCounterStride);
+  // the last tile stages its batch item's partials in the LDS ring
+  const int64_t ring = g.K % t.bk == 0 ? static_cast<int64_t>(t.st) * (t.bm + t.bn) * 2 * t.bk
+                                       : static_cast<int64_t>(kStages) * (t.bm + t.bn) * 2 * kBK;
   g.ticket = B * g.counter_stride * 4 <= kCounterBytes &&
-             tiles_b * g.slots * static_cast<int64_t>(sizeof(float2)) <= kTicketFoldBytes;
+             tiles_b * g.slots * static_cast<int64_t>(sizeof(float2)) <= std::min<int64_t>(ring, kTicketFoldBytes);
   const dim3 grid(static_cast<unsigned>(g.units_per_xcd * kXcds));
   if (g.K % t.bk == 0)
     hipLaunchKernelGGL((gemm_bf16<t.bm, t.bn, t.wgm, t.nw, t.bk, t.st, t.occ, true, true>), grid, dim3(64 * t.nw), 0, st, g);

@@ -32,9 +32,10 @@ class RowShardedResnet:
         sums = torch.stack([ops.dp_groupnorm_sums(x.view(B, -1, self.C), self.G) for x in xs])
         out = []
         for r, x in enumerate(xs):
-            out.append(ops.dp_groupnorm_stale_stats(
-                x.view(B, -1, self.C), sums, r, self.H * self.W, self.wt[f"gamma{i}"], self.wt[f"beta{i}"],
-                self.eps, True, self.G).view_as(x))
+            # the band's own sums are sums[r]; the other bands' are the rest
+            out.append(ops.dp_groupnorm_apply(
+                x.view(B, -1, self.C), sums[r], sums, r, self.H * self.W, self.wt[f"gamma{i}"],
+                self.wt[f"beta{i}"], self.eps, True, self.G).view_as(x))
         return out
 
     def _conv(self, ys: list, i: int) -> list:
