@@ -27,6 +27,8 @@ SIGNATURES = {
     "dp_groupnorm_stale_stats_workspace": (SZ, [I64, I64, I64, I64]),
     "dp_groupnorm_stale_stats": (INT, [P, P, I64, I64, I64, P, P, F32, INT, P, P, I64, I64, I64,
                                        I64, INT, P, SZ, P]),
+    "dp_groupnorm_stale_stats_noalloc": (INT, [P, P, I64, I64, I64, P, P, F32, INT, P, P, I64, I64, I64,
+                                               I64, INT, P]),
     "dp_groupnorm_sums": (INT, [P, P, I64, I64, I64, I64, INT, P, SZ, P]),
     "dp_groupnorm_apply": (INT, [P, P, P, I64, I64, I64, P, P, F32, INT, P, I64, I64, I64, I64, INT, P]),
     "dp_conv3x3_gn_sums_workspace": (SZ, [I64, I64, I64, I64]),

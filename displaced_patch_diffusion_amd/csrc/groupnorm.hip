@@ -28,6 +28,7 @@
 // Every thread owns one 16-byte channel vector of a token, so loads and stores
 // are 16 B wide and consecutive threads touch consecutive bytes.
 #include <algorithm>
+#include <mutex>
 
 #include "dp_internal.h"
 
@@ -783,6 +784,76 @@ DP_API dp_status dp_groupnorm_stale_stats(const void* x, const float* stale_sums
                  reinterpret_cast<float*>(static_cast<char*>(ws) + ws_layout(Bc, T_loc, C, G).coef_off), y, dt, stream);
   }
   return dp::check_launch(name);
+}
+
+// ---------------------------------------------- no-allocation entry point
+// dp_groupnorm_stale_stats_noalloc runs the kernels above with this file-scope
+// device array as their workspace: every device holds its own copy, at its
+// own address, until the process ends.  On the host the array's name denotes
+// a host-side shadow, never the device memory, so host code only ever uses
+// the address hipGetSymbolAddress returns, looked up once per device.  The
+// ticket counters at its start are zeroed by a fill kernel on the first call
+// for a device and are put back to zero by every call's last arrivals; the
+// rest is rewritten before it is read by every call.
+namespace {
+
+constexpr size_t kScratchBytes = size_t(4) << 20;
+constexpr int kMaxDevices = 64;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+__global__ void zero_words(unsigned* p, int n) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0u;
+}
+
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices];
+
+// The current device's copy of `scratch`; the first call for a device looks
+// it up and enqueues the counter region's zero fill on `stream`.
+dp_status device_scratch(const char* name, hipStream_t stream, void** out) {
+  using dp::fail;
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(DP_ERR_HIP, "%s: hipGetDevice: %s", name, hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(DP_ERR_UNSUPPORTED, "%s: device %d beyond the %d devices supported", name, dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(DP_ERR_HIP, "%s: hipGetSymbolAddress: %s", name, hipGetErrorString(e));
+    hipLaunchKernelGGL(zero_words, dim3(8), dim3(256), 0, stream, static_cast<unsigned*>(p), kCounterBytes / 4);
+    e = hipGetLastError();
+    if (e != hipSuccess) return fail(DP_ERR_HIP, "%s: scratch zero fill: %s", name, hipGetErrorString(e));
+    g_scratch[dev] = p;
+  }
+  *out = g_scratch[dev];
+  return DP_OK;
+}
+
+}  // namespace
+
+DP_API dp_status dp_groupnorm_stale_stats_noalloc(const void* x, const float* stale_sums, int64_t n_patches,
+                                                  int64_t rank, int64_t T_total, const float* gamma,
+                                                  const float* beta, float eps, int fuse_silu, void* y,
+                                                  float* fresh_sums_out, int64_t B, int64_t T_loc, int64_t C,
+                                                  int64_t G, dp_dtype dt, hipStream_t stream) {
+  using dp::fail;
+  const char* name = "dp_groupnorm_stale_stats_noalloc";
+  if (!x || !y) return fail(DP_ERR_INVALID_ARG, "%s: NULL x or y", name);
+  GnArgs ga{};
+  dp_status st = check_common(name, x, B, T_loc, C, G, dt, ga);
+  if (st != DP_OK) return st;
+  if ((st = check_stats_args(name, stale_sums, n_patches, rank, T_total, T_loc, eps)) != DP_OK) return st;
+  const size_t need = ws_bytes(B, T_loc, C, G);
+  if (need > kScratchBytes)
+    return fail(DP_ERR_UNSUPPORTED, "%s: the shape needs %zu bytes of scratch, the static scratch holds %zu", name,
+                need, kScratchBytes);
+  void* ws = nullptr;
+  if ((st = device_scratch(name, stream, &ws)) != DP_OK) return st;
+  return dp_groupnorm_stale_stats(x, stale_sums, n_patches, rank, T_total, gamma, beta, eps, fuse_silu, y,
+                                  fresh_sums_out, B, T_loc, C, G, dt, ws, kScratchBytes, stream);
 }
 
 DP_API dp_status dp_groupnorm_sums(const void* x, float* sums_out, int64_t B, int64_t T_loc, int64_t C, int64_t G,

@@ -127,6 +127,23 @@ def dp_groupnorm_stale_stats(x, stale_sums, rank: int, T_total: int, gamma=None,
     return y
 
 
+def dp_groupnorm_stale_stats_noalloc(x, stale_sums, rank: int, T_total: int, gamma, beta, eps: float,
+                                     fuse_silu: bool, G: int, y, fresh_sums_out=None):
+    """dp_groupnorm_stale_stats with the library's static device scratch as
+    its workspace: the call allocates nothing (y is the caller's)."""
+    _dev(x, y, f32=(stale_sums, gamma, beta, fresh_sums_out))
+    dt = _dt(x, y)
+    B, T, C = x.shape
+    n_patches = 1 if stale_sums is None else stale_sums.shape[0]
+    if stale_sums is not None and tuple(stale_sums.shape) != (n_patches, B, G, 2):
+        raise ValueError("stale_sums must be [N,B,G,2]")
+    check(lib().dp_groupnorm_stale_stats_noalloc(_p(x), _p(stale_sums), n_patches, rank, T_total, _p(gamma),
+                                                 _p(beta), float(eps), int(bool(fuse_silu)), _p(y),
+                                                 _p(fresh_sums_out), B, T, C, G, dt, _stream()),
+          "dp_groupnorm_stale_stats_noalloc")
+    return y
+
+
 def dp_groupnorm_sums(x, G: int = 32, out=None, ws=None):
     """x [B,T_loc,C] -> (sum x, sum x^2) per group, [B,G,2] float32."""
     _dev(x, out, ws)

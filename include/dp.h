@@ -177,6 +177,25 @@ dp_status dp_groupnorm_stale_stats(const void* x, const float* stale_sums, int64
                                    hipStream_t stream);
 
 /*
+ * dp_groupnorm_stale_stats without a workspace argument, for callers that
+ * cannot allocate device memory (code under HIP graph capture, serving loops
+ * that allocate nothing per call, harnesses that forbid hipMalloc).  Same
+ * arguments (minus ws/ws_bytes), results and errors; the call allocates
+ * nothing.  Its workspace is a static 4 MiB device array, one per device,
+ * held until the process ends: shapes whose
+ * dp_groupnorm_stale_stats_workspace(...) exceeds 4 MiB are rejected with
+ * DP_ERR_UNSUPPORTED.  Every call on a device shares that device's array:
+ * calls that overlap on one device (different streams, not ordered by the
+ * caller) race and give wrong results.  The first call on a device also
+ * enqueues a small fill kernel on `stream` that zeroes the array's counters.
+ */
+dp_status dp_groupnorm_stale_stats_noalloc(const void* x, const float* stale_sums, int64_t n_patches,
+                                           int64_t rank, int64_t T_total, const float* gamma,
+                                           const float* beta, float eps, int fuse_silu, void* y,
+                                           float* fresh_sums_out, int64_t B, int64_t T_loc, int64_t C,
+                                           int64_t G, dp_dtype dt, hipStream_t stream);
+
+/*
  * Local GroupNorm sums only: the first half of a GroupNorm whose statistics
  * are combined across row bands before normalising (DistVAE row mode,
  * "Benchmarking DistVAE", "Default suite", item 2: adapted layers work on

@@ -284,3 +284,18 @@ def test_size_limits_are_rejected_before_launch(lib):
     # splice with more (batch, K/V) segments than a grid dimension holds
     st, msg = status_and_error(lib.dp_kv_buffer_splice, a, b, c, d, 40_000, 16, 8, 0, 4, bf, None)
     assert st == _lib.DP_ERR_UNSUPPORTED and "grid" in msg
+
+
+def test_groupnorm_noalloc_validation(lib):
+    """The no-allocation GroupNorm rejects bad arguments, and shapes whose
+    workspace exceeds its 4 MiB static scratch, before any HIP call."""
+    def call(x=A, stale=Bp, n=4, rank=1, T_total=4 * 7200, y=Cp, B=2, T=7200, C=640, G=32):
+        return status_and_error(lib.dp_groupnorm_stale_stats_noalloc, x, stale, n, rank, T_total, None, None,
+                                1e-5, 0, y, None, B, T, C, G, _lib.DP_BF16, None)
+
+    assert call(y=None)[0] == _lib.DP_ERR_INVALID_ARG
+    assert call(rank=4)[0] == _lib.DP_ERR_INVALID_ARG
+    assert call(G=7)[0] == _lib.DP_ERR_INVALID_ARG
+    assert lib.dp_groupnorm_stale_stats_workspace(128, 4096, 2048, 2048) > 4 << 20
+    st, msg = call(B=128, T=4096, C=2048, G=2048, T_total=4 * 4096)
+    assert st == _lib.DP_ERR_UNSUPPORTED and "scratch" in msg
