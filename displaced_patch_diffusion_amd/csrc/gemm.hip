@@ -433,6 +433,14 @@ __global__ void __launch_bounds__(64 * NW, OCC) gemm_bf16(GemmArgs g) {
         bq[q][e] = g.bias ? g.bias[min(n0 + wn * WN + 32 * i + 8 * q + 4 * gq + e, g.N - 1)] : 0.f;
   };
 
+  // With GroupNorm sums, the stored outputs also go to an LDS copy of the
+  // tile (the ring is free once every wave is past its last operand read);
+  // rows are padded by 8 bytes so the 32 rows a half-wave writes spread over
+  // the banks.
+  constexpr int kTileStride = BN * 2 + 8;  // bytes per tile row
+  static_assert(!GNS || BM * kTileStride + 2 * BN * 8 <= ST * kStageBytes, "GroupNorm tile copy in LDS");
+  if constexpr (GNS) __syncthreads();
+
   // Epilogue: lane holds rows n = 8*(e/4) + 4*gq + e%4 of column m = l32.
 #pragma unroll
   for (int i = 0; i < NB; ++i) {
@@ -454,57 +462,41 @@ __global__ void __launch_bounds__(64 * NW, OCC) gemm_bf16(GemmArgs g) {
         for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * q + e] + bq[q][e];
         u32x2 packed = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
         *reinterpret_cast<u32x2*>(yrow + n) = packed;
+        if constexpr (GNS) *reinterpret_cast<u32x2*>(lds + (m - m0) * kTileStride + (n - n0) * 2) = packed;
       }
     }
   }
 
   if constexpr (GNS) {
-    // GroupNorm sums of the stored (bf16-rounded) outputs.  Per channel, each
-    // wave sums its rows of the batch item of the tile's first row (segment
-    // 0) and of the next one (segment 1; a tile spans at most two since
-    // gT >= BM): in-lane over its row blocks, then across the 32 lanes of each
-    // half-wave by a fixed butterfly.  The block then sums, in LDS, its waves
-    // and the channels of each group its columns touch, in a fixed order, and
-    // stores one partial per (batch segment, group slot).  The last tile of a
-    // batch item to finish folds that item's partials into gsums.
-    float2* chan = reinterpret_cast<float2*>(lds);  // [2][WGM][BN]
+    // GroupNorm sums of the stored (bf16-rounded) outputs, from the tile copy
+    // in LDS.  A tile spans at most two batch items (segments 0 and 1, since
+    // gT >= BM).  Per channel, one thread sums the rows of each segment in
+    // row order; the block then sums the channels of each group its columns
+    // touch, in a fixed order, and stores one partial per (batch segment,
+    // group slot).  The last tile of a batch item to finish folds that
+    // item's partials into gsums.
+    float2* chan = reinterpret_cast<float2*>(lds + BM * kTileStride);  // [2][BN]
     const int b0 = m0 / g.gT;
-    const int nseg = (min(m0 + BM, g.M) - 1) / g.gT - b0 + 1;
-    const int mw0 = m0 + wm * WM;
-    __syncthreads();  // every wave is past its last operand read of the ring
-    for (int sg = 0; sg < nseg; ++sg) {
-#pragma unroll
-      for (int i = 0; i < NB; ++i) {
-        const int nblk = n0 + wn * WN + 32 * i;
-        float bq[4][4];
-        bias_of(i, bq);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {  // channels nblk + 8q + 4gq + (0..3)
-          float s1[4] = {0.f, 0.f, 0.f, 0.f}, s2[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int j = 0; j < MB; ++j) {
-            const int m = mw0 + 32 * j + l32;
-            const bool on = m < g.M && m / g.gT - b0 == sg && nblk < g.N;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const float y = static_cast<float>(static_cast<__bf16>(acc[i][j][4 * q + e] + bq[q][e]));
-              s1[e] += on ? y : 0.f;
-              s2[e] += on ? y * y : 0.f;
-            }
-          }
-#pragma unroll
-          for (int off = 1; off < 32; off <<= 1)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              s1[e] += __shfl_xor(s1[e], off, 64);
-              s2[e] += __shfl_xor(s2[e], off, 64);
-            }
-          if (l32 == 0) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              chan[(sg * WGM + wm) * BN + wn * WN + 32 * i + 8 * q + 4 * gq + e] = make_float2(s1[e], s2[e]);
-          }
+    const int rows = min(BM, g.M - m0);
+    const int nseg = (m0 + rows - 1) / g.gT - b0 + 1;
+    const int split = min(rows, (b0 + 1) * g.gT - m0);  // rows [0, split) belong to batch item b0
+    __syncthreads();                                     // the tile copy is complete
+    for (int cp = tid; cp < BN / 2; cp += 64 * NW) {
+      const char* col = lds + cp * 4;
+      for (int sg = 0; sg < nseg; ++sg) {
+        float a1 = 0.f, a2 = 0.f, b1 = 0.f, b2 = 0.f;  // channels 2cp and 2cp + 1
+        const int r1 = sg ? rows : split;
+#pragma unroll 4
+        for (int r = sg ? split : 0; r < r1; ++r) {
+          const unsigned int w2 = *reinterpret_cast<const unsigned int*>(col + r * kTileStride);
+          const float y0 = bf16_lo(w2), y1 = bf16_hi(w2);
+          a1 += y0;
+          a2 = fmaf(y0, y0, a2);
+          b1 += y1;
+          b2 = fmaf(y1, y1, b2);
         }
+        chan[sg * BN + 2 * cp] = make_float2(a1, a2);
+        chan[sg * BN + 2 * cp + 1] = make_float2(b1, b2);
       }
     }
     __syncthreads();
@@ -520,13 +512,11 @@ __global__ void __launch_bounds__(64 * NW, OCC) gemm_bf16(GemmArgs g) {
         if (st < nseg * nslots) {
           const int sg = st / nslots, jj = st - sg * nslots, gi = g_lo + jj;
           const int c0 = max(gi * g.Cg, n0), c1 = min((gi + 1) * g.Cg, n1);
-          for (int c = c0 + l; c < c1; c += sl)
-#pragma unroll
-            for (int w = 0; w < WGM; ++w) {
-              const float2 v = chan[(sg * WGM + w) * BN + c - n0];
-              acc2.x += v.x;
-              acc2.y += v.y;
-            }
+          for (int c = c0 + l; c < c1; c += sl) {
+            const float2 v = chan[sg * BN + c - n0];
+            acc2.x += v.x;
+            acc2.y += v.y;
+          }
         }
         acc2 = lane_sum(acc2, sl);
         if (st < nseg * nslots && l == 0) {

@@ -26,9 +26,15 @@
  *    non-OK return has enqueued nothing and written nothing), then work is
  *    enqueued on `stream` and the call returns.  Faults during execution
  *    surface at the caller's next synchronisation of that stream.
- *  - The library holds no state between calls apart from a thread-local
- *    error string.  Calls on one stream are ordered; concurrent calls on
- *    different streams must not share output buffers or workspaces.
+ *  - State kept between calls, none of it caller data: the calling thread's
+ *    last-error string; per device, a zero-filled 4 KiB device page the conv
+ *    reads in place of absent halo rows and columns outside the image; per
+ *    thread, each device's CU count and the attention kernels' resident
+ *    blocks per CU, asked of the runtime once; per device, the 4 MiB scratch
+ *    of dp_groupnorm_stale_stats_noalloc and its address.  The environment
+ *    variable DP_ATTN_SCHEDULE is read at every attention call and query.
+ *    Calls on one stream are ordered; concurrent calls on different streams
+ *    must not share output buffers or workspaces.
  */
 #ifndef DP_H_
 #define DP_H_
@@ -87,13 +93,17 @@ dp_status dp_kv_buffer_splice(void* k_buf, void* v_buf, const void* k_fresh, con
  * q     [B, Tq, H*d];  k_buf, v_buf [B, T_kv, H*d];  out [B, Tq, H*d].
  * scale <= 0 selects 1/sqrt(d).  Softmax and accumulation run in float32;
  * in bf16 the probabilities are rounded to bf16 before the P*V product.
+ * q, k_buf and v_buf must hold finite values: the bf16 kernel fixes each
+ * row's softmax reference from its first key block and moves it only when a
+ * later block's row sum overflows, so a NaN or infinite input gives an
+ * undefined output rather than a propagated NaN.
  * Supported: bf16 with d = 64; f32 with d in {32, 64}.
  * ws/ws_bytes: caller-owned device scratch of at least
  * dp_attn_stale_kv_workspace(...) bytes (NULL allowed when that is 0).  The
- * size depends on the work schedule the library picks for the shape (and on
- * the device's CU count); DP_ATTN_SCHEDULE=split or =balanced in the
- * environment overrides that pick, so the query and the call must run with
- * the same setting.
+ * library picks one of two work schedules per shape (and per the device's CU
+ * count); DP_ATTN_SCHEDULE=split or =balanced in the environment, read at
+ * every call, forces one (tests and tuning).  The queried size covers both
+ * schedules, so the setting never makes a queried workspace too small.
  * Errors: INVALID_ARG for NULL pointers, sizes <= 0 or a workspace that is too
  * small; UNSUPPORTED for other d or dtype combinations.
  */
@@ -134,10 +144,13 @@ dp_status dp_conv3x3_stale_halo(const void* x, const void* halo_top, const void*
  * tile in the conv epilogue and folded in a fixed order (deterministic; equal
  * to dp_groupnorm_sums of y up to float32 rounding order).
  * gn_sums [B, G, 2] float32; ws/ws_bytes: caller-owned device scratch of at
- * least dp_conv3x3_gn_sums_workspace(B, h, W, Cout) bytes; other arguments as
+ * least dp_conv3x3_gn_sums_workspace(B, h, W, Cout) bytes, zero-filled by the
+ * caller before its first use (its first 32 KiB hold ticket counters that
+ * every call leaves at zero again, so one zero fill serves any later calls
+ * and shapes, on one stream at a time); other arguments as
  * dp_conv3x3_stale_halo.
- * Supported: bf16 with Cin % 32 == 0, Cin <= 2048, Cout % 32 == 0 and
- * h*W >= 160.  Errors: INVALID_ARG for NULL x/w/y/gn_sums, sizes <= 0,
+ * Supported: bf16 with Cin % 32 == 0, Cin <= 2048, Cout % 32 == 0,
+ * Cout <= 2048 and h*W >= 160.  Errors: INVALID_ARG for NULL x/w/y/gn_sums, sizes <= 0,
  * Cout % G != 0, a short workspace or overlapping buffers; UNSUPPORTED
  * otherwise (f32 included: use dp_conv3x3_stale_halo then dp_groupnorm_sums).
  */
@@ -162,7 +175,10 @@ dp_status dp_conv3x3_stale_halo_gn_sums(const void* x, const void* halo_top, con
  * x [B, T_loc, C]; stale_sums [n_patches, B, G, 2] float32, entry [rank] is
  * never read; gamma, beta [C] float32 or NULL (1 and 0); y [B, T_loc, C];
  * fresh_sums_out [B, G, 2] float32 receives the local sums, or NULL.
- * ws/ws_bytes: at least dp_groupnorm_stale_stats_workspace(...) bytes.
+ * ws/ws_bytes: at least dp_groupnorm_stale_stats_workspace(...) bytes,
+ * zero-filled by the caller before its first use (its first 32 KiB hold
+ * ticket counters that every call leaves at zero again, so one zero fill
+ * serves any later calls and shapes, on one stream at a time).
  * Supported: C % G == 0, C % 8 == 0 (bf16) or C % 4 == 0 (f32), C <= 2048.
  * Errors: INVALID_ARG for NULL x/y/stale_sums (stale_sums may be NULL only
  * when n_patches == 1), sizes <= 0, rank outside [0, n_patches), T_total < T_loc,
