@@ -555,7 +555,8 @@ def measure_ops(torch, share, K: int, reps: int, flush):
     for name, fn in share.ops_:
         b2b[name] = b2b.get(name, 0.0) + back_to_back_us(torch, fn, K)
         hot[name] = hot.get(name, 0.0) + event_medians_us(torch, fn, reps)
-        cold[name] = cold.get(name, 0.0) + event_medians_us(torch, fn, reps, flush)
+        if flush is not None:
+            cold[name] = cold.get(name, 0.0) + event_medians_us(torch, fn, reps, flush)
     return b2b, hot, cold
 
 
@@ -564,15 +565,17 @@ def kernel_table(w, b2b, hot, cold):
     peak_mfma = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
     kern = {}
     for name, t in b2b.items():
-        rec = {"us": round(t, 2), "us_hot_median": round(hot[name], 2), "us_cold_median": round(cold[name], 2)}
+        c = cold.get(name)
+        rec = {"us": round(t, 2), "us_hot_median": round(hot[name], 2),
+               "us_cold_median": None if c is None else round(c, 2)}
         if name in fl:
             a = fl[name] / t / 1e6
             rec.update({"TFLOP/s": round(a, 1), "frac": round(a / peak_mfma, 4),
-                        "frac_cold": round(fl[name] / cold[name] / 1e6 / peak_mfma, 4)})
+                        "frac_cold": None if c is None else round(fl[name] / c / 1e6 / peak_mfma, 4)})
         elif name in by:
             a = by[name] / t / 1e3
             rec.update({"GB/s": round(a, 1), "frac": round(a / PEAK_HBM_GBPS, 4),
-                        "frac_cold": round(by[name] / cold[name] / 1e3 / PEAK_HBM_GBPS, 4)})
+                        "frac_cold": None if c is None else round(by[name] / c / 1e3 / PEAK_HBM_GBPS, 4)})
         kern[name] = rec
     return kern
 
@@ -583,11 +586,11 @@ def splice_timing(torch, ops, share, K: int, reps: int, flush):
     w = share.w
     fn = lambda: ops.dp_kv_buffer_splice(share.k_buf, share.v_buf, share.kf, share.vf, share.t0)
     t = back_to_back_us(torch, fn, K)
-    cold = event_medians_us(torch, fn, reps, flush)
+    cold = event_medians_us(torch, fn, reps, flush) if flush is not None else None
     by = w.bytes()["splice"]
     return {"us": round(t, 2), "GB/s": round(by / t / 1e3, 1), "frac": round(by / t / 1e3 / PEAK_HBM_GBPS, 4),
-            "us_cold_median": round(cold, 2), "frac_cold": round(by / cold / 1e3 / PEAK_HBM_GBPS, 4),
-            "bytes": by}
+            "us_cold_median": None if cold is None else round(cold, 2),
+            "frac_cold": None if cold is None else round(by / cold / 1e3 / PEAK_HBM_GBPS, 4), "bytes": by}
 
 
 def config_summary(torch, ops, synth, name: str, K: int, reps: int, flush):
@@ -600,10 +603,11 @@ def config_summary(torch, ops, synth, name: str, K: int, reps: int, flush):
     b2b, hot, cold = measure_ops(torch, share, K, reps, flush)
     step = lambda: share.step(lambda n: None)
     step_hot = event_medians_us(torch, step, reps)
-    step_cold = event_medians_us(torch, step, reps, flush)
+    step_cold = event_medians_us(torch, step, reps, flush) if flush is not None else None
     fl = w.flops()
     out = {"workload": w.name, "note": w.note, "dtype": w.dtype,
-           "step_us_hot_median": round(step_hot, 2), "step_us_cold_median": round(step_cold, 2),
+           "step_us_hot_median": round(step_hot, 2),
+           "step_us_cold_median": None if step_cold is None else round(step_cold, 2),
            "TFLOP/s_hot": round(sum(fl.values()) / step_hot / 1e6, 1),
            "kernels": kernel_table(w, b2b, hot, cold)}
     if w.dtype == "bf16":
@@ -708,6 +712,11 @@ def main():
     ap.add_argument("--no-otil", action="store_true", help="skip the OTIL selective-transmit timing")
     ap.add_argument("--no-vae", action="store_true", help="skip the row-sharded VAE decoder timing")
     ap.add_argument("--no-configs", action="store_true", help="skip the other bf16 workloads' numbers")
+    ap.add_argument("--seed", type=int, default=0,
+                    help="another family of seeded input streams (0: the one the tests use)")
+    ap.add_argument("--noise", type=float, default=None, help="std of the stale-state noise (default: the workload's)")
+    ap.add_argument("--rank", type=int, default=None, help="which rank's share to time (default: the workload's)")
+    ap.add_argument("--no-flush", action="store_true", help="skip the cold (cache-flushed) medians")
     ap.add_argument("--profile-ops", type=int, default=0, metavar="R",
                     help="rocprofv3 mode: launch each op of the step R times in step order, spin kernels "
                          "between the ops, print the op labels and exit (no timing)")
@@ -731,6 +740,13 @@ def main():
     if args.workload not in synth.WORKLOADS:
         sys.exit(f"unknown workload {args.workload}; choose from {list(synth.WORKLOADS)}")
     w = synth.WORKLOADS[args.workload]
+    if args.rank is not None:
+        if not 0 <= args.rank < w.N:
+            sys.exit(f"--rank must be in [0, {w.N}) for {w.name}")
+        w = w.with_rank(args.rank)
+    if args.noise is not None:
+        w = w.with_noise(args.noise)
+    synth.set_stream_salt(args.seed)
     torch.cuda.set_device(0)
     log(f"bench: workload {w.name}: building inputs")
     share = make_share(w, args.qkv, args.gn_sums)
@@ -751,7 +767,7 @@ def main():
                                            "qkv": args.qkv, "gn_sums": args.gn_sums,
                                            "splice_bytes": w.bytes()["splice"]}), flush=True)
         return
-    flush = Flusher(torch)
+    flush = None if args.no_flush else Flusher(torch)
     K, R = args.steps, args.reps
     # Per-op breakdown, before the timed steps: the back-to-back average of K
     # launches of each op (behind a GPU spin that lets the host queue them
@@ -786,7 +802,7 @@ def main():
     # the whole step's medians, after the timed region
     step = lambda: share.step(lambda n: None)
     step_hot = event_medians_us(torch, step, R)
-    step_cold = event_medians_us(torch, step, R, flush)
+    step_cold = event_medians_us(torch, step, R, flush) if flush is not None else None
 
     fl = w.flops()
     step_s = wall / K
@@ -810,13 +826,15 @@ def main():
                    "C_attn": w.attn_C, "heads": w.heads, "head_dim": w.head_dim,
                    "conv_level": f"{w.conv_H}x{w.conv_W}", "C_conv": w.conv_C, "n_patches": w.N,
                    "rank": w.rank, "Tq": w.Tq, "T_kv": w.T_kv, "qkv": args.qkv, "gn_sums": args.gn_sums,
+                   "noise": w.noise, "seed": args.seed,
                    "parallelism": "one rank's share, 1 GPU"},
         "roofline": roofline,
         "kernels": kern,
         "groupnorm_GBps": kern.get("groupnorm", {}).get("GB/s"),
         "splice": splice,
-        "step_us_hot_median": round(step_hot, 2), "step_us_cold_median": round(step_cold, 2),
-        "timing": {"reps": R, "flush_bytes": Flusher.BYTES,
+        "step_us_hot_median": round(step_hot, 2),
+        "step_us_cold_median": None if step_cold is None else round(step_cold, 2),
+        "timing": {"reps": R, "flush_bytes": None if flush is None else Flusher.BYTES,
                    "per_op_us": "average of K back-to-back launches (hot)",
                    "medians": "median of reps single launches between an event pair; cold reps flush "
                               "the caches with a 1 GiB write outside the pair"},

@@ -192,8 +192,21 @@ WORKLOAD_ORDER = list(WORKLOADS)
 
 
 # --------------------------------------------------------------------- drawing
+_SALT = 0
+
+
+def set_stream_salt(salt: int) -> None:
+    """Select another family of streams (0, the default, is the one every
+    test and stored value uses); the benchmark's --seed sets it."""
+    global _SALT
+    if salt < 0:
+        raise ValueError("the salt must be >= 0")
+    _SALT = int(salt)
+
+
 def _rng(seed: int, name: str) -> np.random.Generator:
-    return np.random.default_rng(np.random.SeedSequence([seed, zlib.crc32(name.encode())]))
+    key = [seed, zlib.crc32(name.encode())] + ([_SALT] if _SALT else [])
+    return np.random.default_rng(np.random.SeedSequence(key))
 
 
 def normal(seed: int, name: str, shape, std: float = 1.0, mean: float = 0.0) -> np.ndarray:

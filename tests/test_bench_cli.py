@@ -22,3 +22,21 @@ def test_world_size_above_one_exits_with_a_message():
     env = dict(os.environ, WORLD_SIZE="2")
     r = run("--gpus", "1", env=env)
     assert r.returncode == 2 and "WORLD_SIZE=2" in r.stderr
+
+
+def test_rank_outside_the_workload_is_rejected():
+    r = run("--rank", "9")
+    assert r.returncode != 0 and "--rank must be in [0, 8)" in r.stderr
+
+
+def test_stream_salt_selects_other_streams_and_zero_restores_them():
+    from displaced_patch_diffusion_amd import synth
+
+    base = synth.normal(1, "salt.check", (8,))
+    try:
+        synth.set_stream_salt(3)
+        other = synth.normal(1, "salt.check", (8,))
+    finally:
+        synth.set_stream_salt(0)
+    assert not (other == base).all()
+    assert (synth.normal(1, "salt.check", (8,)) == base).all()
