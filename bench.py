@@ -270,6 +270,12 @@ class Share:
                     self.G, y=self.gc[0], fresh_sums_out=self.fresh[0], ws=self.gn_ws)))
         return L
 
+    def outputs(self):
+        """Tensors the step writes and no op reads before writing (the K/V
+        buffers, updated in place, are left out)."""
+        n = 2 if self.w.two_level else 1
+        return [self.q, self.o, self.y, *self.zc[:n], *self.gc[:n], *self.fresh[:n]]
+
     # one step; `mark(name)` is called after each op is enqueued
     def step(self, mark):
         for name, fn in self.ops_:
@@ -612,9 +618,45 @@ def config_summary(torch, ops, synth, name: str, K: int, reps: int, flush):
            "kernels": kernel_table(w, b2b, hot, cold)}
     if w.dtype == "bf16":
         out["splice"] = splice_timing(torch, ops, share, K, reps, flush)
+    out["graph"] = graph_timing(torch, share, K, reps, flush)
     del share
     torch.cuda.empty_cache()
     return out
+
+
+def graph_timing(torch, share, K: int, reps: int, flush):
+    """The step captured once as a HIP graph (torch.cuda.CUDAGraph) and
+    replayed: back-to-back average and hot/cold medians per replay.  Before
+    timing, three replays, each after the step's outputs were cleared by eager
+    work, must reproduce the eager step's outputs bit for bit."""
+    noop = lambda n: None
+    try:
+        outs = share.outputs()
+        share.step(noop)
+        torch.cuda.synchronize()
+        ref = [t.clone() for t in outs]
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            share.step(noop)
+        torch.cuda.synchronize()
+        match = True
+        for _ in range(3):
+            for t in outs:
+                t.zero_()
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            match = match and all(torch.equal(a, b) for a, b in zip(outs, ref))
+        if not match:
+            return {"replays_match_eager": False}
+        t = back_to_back_us(torch, g.replay, K)
+        hot = event_medians_us(torch, g.replay, reps)
+        cold = event_medians_us(torch, g.replay, reps, flush) if flush is not None else None
+        del g
+        return {"replays_match_eager": True, "step_us": round(t, 2), "step_us_hot_median": round(hot, 2),
+                "step_us_cold_median": None if cold is None else round(cold, 2)}
+    except Exception as e:  # capture not available: reported, not fatal
+        return {"error": f"{type(e).__name__}: {e}"}
 
 
 # ------------------------------------------------------------ profile runs
@@ -817,6 +859,8 @@ def main():
                 "traffic": _traffic_from_profile(w), "kernel": "attn_bf16_d64",
                 "work_per_launch": f"{fl['attn'] / 1e9:.2f} GFLOP"}
     splice = splice_timing(torch, ops, share, K, R, flush) if w.dtype == "bf16" else None
+    log("bench: the step as a HIP graph")
+    graph = graph_timing(torch, share, K, R, flush)
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": K, "warmup": args.warmup, "ms_per_step": round(step_s * 1e3, 4),
@@ -832,6 +876,7 @@ def main():
         "kernels": kern,
         "groupnorm_GBps": kern.get("groupnorm", {}).get("GB/s"),
         "splice": splice,
+        "graph": graph,
         "step_us_hot_median": round(step_hot, 2),
         "step_us_cold_median": None if step_cold is None else round(step_cold, 2),
         "timing": {"reps": R, "flush_bytes": None if flush is None else Flusher.BYTES,
