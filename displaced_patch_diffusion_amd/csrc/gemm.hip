@@ -438,7 +438,10 @@ __global__ void __launch_bounds__(64 * NW, OCC) gemm_bf16(GemmArgs g) {
   // rows are padded by 8 bytes so the 32 rows a half-wave writes spread over
   // the banks.
   constexpr int kTileStride = BN * 2 + 8;  // bytes per tile row
-  static_assert(!GNS || BM * kTileStride + 2 * BN * 8 <= ST * kStageBytes, "GroupNorm tile copy in LDS");
+  // column sums: one thread per channel pair and row part
+  constexpr int kPairs = BN / 2, kParts = (64 * NW) / kPairs > 0 ? (64 * NW) / kPairs : 1;
+  static_assert(!GNS || BM * kTileStride + (2 + 2 * kParts) * BN * 8 <= ST * kStageBytes,
+                "GroupNorm tile copy in LDS");
   if constexpr (GNS) __syncthreads();
 
   // Epilogue: lane holds rows n = 8*(e/4) + 4*gq + e%4 of column m = l32.
@@ -470,34 +473,53 @@ __global__ void __launch_bounds__(64 * NW, OCC) gemm_bf16(GemmArgs g) {
   if constexpr (GNS) {
     // GroupNorm sums of the stored (bf16-rounded) outputs, from the tile copy
     // in LDS.  A tile spans at most two batch items (segments 0 and 1, since
-    // gT >= BM).  Per channel, one thread sums the rows of each segment in
-    // row order; the block then sums the channels of each group its columns
-    // touch, in a fixed order, and stores one partial per (batch segment,
-    // group slot).  The last tile of a batch item to finish folds that
-    // item's partials into gsums.
+    // gT >= BM).  Per channel pair and row part, one thread sums its rows of
+    // each segment in row order; the parts are then added in part order, the
+    // block sums the channels of each group its columns touch, in a fixed
+    // order, and stores one partial per (batch segment, group slot).  The
+    // last tile of a batch item to finish folds that item's partials into
+    // gsums.
     float2* chan = reinterpret_cast<float2*>(lds + BM * kTileStride);  // [2][BN]
+    float2* parts = chan + 2 * BN;                                     // [kParts][2][BN]
     const int b0 = m0 / g.gT;
     const int rows = min(BM, g.M - m0);
     const int nseg = (m0 + rows - 1) / g.gT - b0 + 1;
     const int split = min(rows, (b0 + 1) * g.gT - m0);  // rows [0, split) belong to batch item b0
     __syncthreads();                                     // the tile copy is complete
-    for (int cp = tid; cp < BN / 2; cp += 64 * NW) {
-      const char* col = lds + cp * 4;
-      for (int sg = 0; sg < nseg; ++sg) {
-        float a1 = 0.f, a2 = 0.f, b1 = 0.f, b2 = 0.f;  // channels 2cp and 2cp + 1
-        const int r1 = sg ? rows : split;
+    {
+      const int cp = tid % kPairs, pi = tid / kPairs;
+      if (pi < kParts) {
+        const char* col = lds + cp * 4;
+        for (int sg = 0; sg < nseg; ++sg) {
+          const int ra = sg ? split : 0, rb = sg ? rows : split;
+          const int len = (rb - ra + kParts - 1) / kParts;
+          const int r0 = ra + pi * len, r1 = min(rb, r0 + len);
+          float a1 = 0.f, a2 = 0.f, b1 = 0.f, b2 = 0.f;  // channels 2cp and 2cp + 1
 #pragma unroll 4
-        for (int r = sg ? split : 0; r < r1; ++r) {
-          const unsigned int w2 = *reinterpret_cast<const unsigned int*>(col + r * kTileStride);
-          const float y0 = bf16_lo(w2), y1 = bf16_hi(w2);
-          a1 += y0;
-          a2 = fmaf(y0, y0, a2);
-          b1 += y1;
-          b2 = fmaf(y1, y1, b2);
+          for (int r = r0; r < r1; ++r) {
+            const unsigned int w2 = *reinterpret_cast<const unsigned int*>(col + r * kTileStride);
+            const float y0 = bf16_lo(w2), y1 = bf16_hi(w2);
+            a1 += y0;
+            a2 = fmaf(y0, y0, a2);
+            b1 += y1;
+            b2 = fmaf(y1, y1, b2);
+          }
+          parts[(pi * 2 + sg) * BN + 2 * cp] = make_float2(a1, a2);
+          parts[(pi * 2 + sg) * BN + 2 * cp + 1] = make_float2(b1, b2);
         }
-        chan[sg * BN + 2 * cp] = make_float2(a1, a2);
-        chan[sg * BN + 2 * cp + 1] = make_float2(b1, b2);
       }
+    }
+    __syncthreads();
+    for (int e = tid; e < nseg * BN; e += 64 * NW) {
+      const int sg = e / BN, c = e - sg * BN;
+      float2 acc2 = make_float2(0.f, 0.f);
+#pragma unroll
+      for (int p = 0; p < kParts; ++p) {
+        const float2 v = parts[(p * 2 + sg) * BN + c];
+        acc2.x += v.x;
+        acc2.y += v.y;
+      }
+      chan[sg * BN + c] = acc2;
     }
     __syncthreads();
     const int n1 = min(n0 + BN, g.N);
