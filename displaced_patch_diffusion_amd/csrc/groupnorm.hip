@@ -850,6 +850,10 @@ DP_API dp_status dp_groupnorm_stale_stats_noalloc(const void* x, const float* st
   if (need > kScratchBytes)
     return fail(DP_ERR_UNSUPPORTED, "%s: the shape needs %zu bytes of scratch, the static scratch holds %zu", name,
                 need, kScratchBytes);
+  // every check of the workspace entry point is done here too, before the
+  // first call's zero fill may be enqueued: a non-OK return enqueues nothing
+  const size_t xb = static_cast<size_t>(B * T_loc * C) * dp::dtype_size(dt);
+  if (dp::overlaps(x, xb, y, xb)) return fail(DP_ERR_INVALID_ARG, "%s: x and y overlap", name);
   void* ws = nullptr;
   if ((st = device_scratch(name, stream, &ws)) != DP_OK) return st;
   return dp_groupnorm_stale_stats(x, stale_sums, n_patches, rank, T_total, gamma, beta, eps, fuse_silu, y,

@@ -299,3 +299,6 @@ def test_groupnorm_noalloc_validation(lib):
     assert lib.dp_groupnorm_stale_stats_workspace(128, 4096, 2048, 2048) > 4 << 20
     st, msg = call(B=128, T=4096, C=2048, G=2048, T_total=4 * 4096)
     assert st == _lib.DP_ERR_UNSUPPORTED and "scratch" in msg
+    # overlapping x and y: rejected before the first call's scratch set-up
+    st, msg = call(y=A + 2)
+    assert st == _lib.DP_ERR_INVALID_ARG and "overlap" in msg
