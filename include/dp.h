@@ -203,7 +203,10 @@ dp_status dp_groupnorm_stale_stats(const void* x, const float* stale_sums, int64
  * DP_ERR_UNSUPPORTED.  Every call on a device shares that device's array:
  * calls that overlap on one device (different streams, not ordered by the
  * caller) race and give wrong results.  The first call on a device also
- * enqueues a small fill kernel on `stream` that zeroes the array's counters.
+ * looks up the array's address and enqueues a small fill kernel on `stream`
+ * that zeroes its counters; a caller that captures the call in a HIP graph
+ * makes one call before capturing, so that this set-up stays outside the
+ * graph.
  */
 dp_status dp_groupnorm_stale_stats_noalloc(const void* x, const float* stale_sums, int64_t n_patches,
                                            int64_t rank, int64_t T_total, const float* gamma,

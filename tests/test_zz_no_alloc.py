@@ -43,3 +43,31 @@ def test_noalloc_matches_workspace_entry(calls):
         torch.cuda.synchronize()
         assert torch.equal(f, f_ref), f"call {i}: fresh sums differ"
         assert torch.equal(y, y_ref), f"call {i}: outputs differ"
+
+
+def test_noalloc_replays_in_a_hip_graph():
+    """The callers it is for: the call captured in a HIP graph (after one
+    eager call, which does the per-device set-up) and replayed three times
+    with eager work in between; every replay equals the workspace entry
+    point's output."""
+    dt, B, T, C, G, N, rank = "bf16", 2, 2000, 320, 32, 4, 2
+    print(f"no-alloc graph: {dt} B={B} T={T} C={C} G={G}", file=sys.stderr, flush=True)
+    x, stale, gamma, beta = _case(20, dt, B, T, C, G, N, rank, True)
+    y_ref = torch.empty_like(x)
+    f_ref = torch.empty((B, G, 2), dtype=torch.float32, device="cuda")
+    ops.dp_groupnorm_stale_stats(x, stale, rank, N * T, gamma, beta, 1e-5, True, G, y=y_ref, fresh_sums_out=f_ref)
+    y, f = torch.empty_like(x), torch.empty_like(f_ref)
+    ops.dp_groupnorm_stale_stats_noalloc(x, stale, rank, N * T, gamma, beta, 1e-5, True, G, y, fresh_sums_out=f)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        ops.dp_groupnorm_stale_stats_noalloc(x, stale, rank, N * T, gamma, beta, 1e-5, True, G, y, fresh_sums_out=f)
+    torch.cuda.synchronize()
+    for i in range(3):
+        y.fill_(float("nan"))
+        f.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(f, f_ref), f"replay {i}: fresh sums differ"
+        assert torch.equal(y, y_ref), f"replay {i}: outputs differ"
