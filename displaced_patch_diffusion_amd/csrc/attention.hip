@@ -832,6 +832,8 @@ DP_API dp_status dp_attn_stale_kv(const void* q, const void* k_buf, const void* 
                 (long long)d);
   if (Tq > 0x7FFFFFFF || T_kv > 0x7FFFFFFF || H > 65535 || B > 65535)
     return fail(DP_ERR_UNSUPPORTED, "dp_attn_stale_kv: size exceeds grid limits");
+  if (dt == DP_BF16 && (!dp::aligned16(q) || !dp::aligned16(k_buf) || !dp::aligned16(v_buf) || !dp::aligned16(out)))
+    return fail(DP_ERR_INVALID_ARG, "dp_attn_stale_kv: q, k_buf, v_buf and out must be 16-byte aligned");
   const float sc = scale > 0.f ? scale : static_cast<float>(1.0 / sqrt(static_cast<double>(d)));
   dp::clear_error();
   if (dt == DP_BF16) {

@@ -25,6 +25,9 @@ inline bool overlaps(const void* a, size_t an, const void* b, size_t bn) {
 }
 
 inline size_t dtype_size(dp_dtype dt) { return dt == DP_BF16 ? 2 : 4; }
+
+// The vector kernels move activations, weights and outputs in 16-byte pieces.
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 inline bool dtype_ok(dp_dtype dt) { return dt == DP_BF16 || dt == DP_F32; }
 
 }  // namespace dp

@@ -433,40 +433,51 @@ __global__ void __launch_bounds__(64 * NW, OCC) gemm_bf16(GemmArgs g) {
         bq[q][e] = g.bias ? g.bias[min(n0 + wn * WN + 32 * i + 8 * q + 4 * gq + e, g.N - 1)] : 0.f;
   };
 
-  // With GroupNorm sums, the stored outputs also go to an LDS copy of the
-  // tile (the ring is free once every wave is past its last operand read);
-  // rows are padded by 8 bytes so the 32 rows a half-wave writes spread over
-  // the banks.
-  constexpr int kTileStride = BN * 2 + 8;  // bytes per tile row
-  // column sums: one thread per channel pair and row part
+  // Epilogue through LDS.  Each wave's accumulators hold 4 consecutive
+  // channels of one output row per lane, so stores straight from registers
+  // write 16 bytes to each of 32 rows per instruction: partial cache lines,
+  // which cost a third of a short-K projection.  Instead the tile (bias
+  // added, rounded to bf16) goes to LDS (the ring is free once every wave is
+  // past its last operand read), rows padded by 16 bytes, and leaves in
+  // 16-byte chunks, consecutive threads on consecutive chunks of a row.
+  constexpr int kTileStride = BN * 2 + 16;  // bytes per tile row
+  // GroupNorm column sums: one thread per channel pair and row part
   constexpr int kPairs = BN / 2, kParts = (64 * NW) / kPairs > 0 ? (64 * NW) / kPairs : 1;
-  static_assert(!GNS || BM * kTileStride + (2 + 2 * kParts) * BN * 8 <= ST * kStageBytes,
-                "GroupNorm tile copy in LDS");
-  if constexpr (GNS) __syncthreads();
+  static_assert(BM * kTileStride + (GNS ? (2 + 2 * kParts) * BN * 8 : 0) <= ST * kStageBytes,
+                "output tile in LDS");
+  __syncthreads();
 
-  // Epilogue: lane holds rows n = 8*(e/4) + 4*gq + e%4 of column m = l32.
+  // lane holds rows n = 8*(e/4) + 4*gq + e%4 of column m = l32
 #pragma unroll
   for (int i = 0; i < NB; ++i) {
     float bq[4][4];
     bias_of(i, bq);
 #pragma unroll
     for (int j = 0; j < MB; ++j) {
-      const int m = m0 + wm * WM + 32 * j + l32;
-      const int nblk = n0 + wn * WN + 32 * i;
-      if (m >= g.M || nblk >= g.N) continue;
-      const int seg = nblk / g.map.seg_n;  // a 32-column block lies in one segment
-      bf16_t* yrow = static_cast<bf16_t*>(g.map.outs[seg]) + out_row(g.map, seg, m) * g.map.seg_n -
-                     seg * g.map.seg_n;
+      const int ml = wm * WM + 32 * j + l32;
+      const int nl = wn * WN + 32 * i;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int n = nblk + 8 * q + 4 * gq;
         float v[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * q + e] + bq[q][e];
-        u32x2 packed = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-        *reinterpret_cast<u32x2*>(yrow + n) = packed;
-        if constexpr (GNS) *reinterpret_cast<u32x2*>(lds + (m - m0) * kTileStride + (n - n0) * 2) = packed;
+        const u32x2 packed = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+        *reinterpret_cast<u32x2*>(lds + ml * kTileStride + (nl + 8 * q + 4 * gq) * 2) = packed;
       }
+    }
+  }
+  __syncthreads();
+  {
+    constexpr int kChunks = BN / 8;  // 16-byte chunks per tile row
+    const int rows = min(BM, g.M - m0), cols = min(BN, g.N - n0);
+    for (int e = tid; e < rows * kChunks; e += 64 * NW) {
+      const int r = e / kChunks, c = (e - r * kChunks) * 8;
+      if (c >= cols) continue;
+      const int m = m0 + r, n = n0 + c;
+      const int seg = n / g.map.seg_n;  // 8 channels never straddle a segment (seg_n % 32 == 0)
+      bf16_t* yrow = static_cast<bf16_t*>(g.map.outs[seg]) + out_row(g.map, seg, m) * g.map.seg_n -
+                     seg * g.map.seg_n;
+      *reinterpret_cast<u32x4*>(yrow + n) = *reinterpret_cast<const u32x4*>(lds + r * kTileStride + c * 2);
     }
   }
 
@@ -485,7 +496,6 @@ __global__ void __launch_bounds__(64 * NW, OCC) gemm_bf16(GemmArgs g) {
     const int rows = min(BM, g.M - m0);
     const int nseg = (m0 + rows - 1) / g.gT - b0 + 1;
     const int split = min(rows, (b0 + 1) * g.gT - m0);  // rows [0, split) belong to batch item b0
-    __syncthreads();                                     // the tile copy is complete
     {
       const int cp = tid % kPairs, pi = tid / kPairs;
       if (pi < kParts) {
@@ -831,6 +841,11 @@ dp_status run_gemm(bool conv, const void* a, const void* x, const void* ht, cons
                    int64_t K, dp_dtype dt, hipStream_t st, const char* name) {
   if (M > 0x7FFFFFFF || N > 0x7FFFFFFF || K > 0x7FFFFFFF)
     return dp::fail(DP_ERR_UNSUPPORTED, "%s: dimension exceeds 2^31", name);
+  if (dt == DP_BF16) {
+    bool al = dp::aligned16(conv ? x : a) && (!ht || dp::aligned16(ht)) && (!hb || dp::aligned16(hb));
+    for (int s = 0; s < map.n_seg; ++s) al = al && dp::aligned16(map.wts[s]) && dp::aligned16(map.outs[s]);
+    if (!al) return dp::fail(DP_ERR_INVALID_ARG, "%s: bf16 tensors must be 16-byte aligned", name);
+  }
   dp::clear_error();
   if (dt == DP_BF16) {
     if (K % kBK != 0 || map.seg_n % 32 != 0 || (conv && (Cin % kBK != 0 || Cin > 2048)))
@@ -997,6 +1012,9 @@ DP_API dp_status dp_conv3x3_stale_halo_gn_sums(const void* x, const void* halo_t
     return fail(DP_ERR_UNSUPPORTED, "%s: needs bf16 with Cin %% 32 == 0, Cin <= 2048, Cout %% 32 == 0, Cout <= 2048",
                 name);
   if (h * W < 160) return fail(DP_ERR_UNSUPPORTED, "%s: needs at least 160 tokens per batch item", name);
+  if (!dp::aligned16(x) || !dp::aligned16(w) || !dp::aligned16(y) || (halo_top && !dp::aligned16(halo_top)) ||
+      (halo_bot && !dp::aligned16(halo_bot)))
+    return fail(DP_ERR_INVALID_ARG, "%s: bf16 tensors must be 16-byte aligned", name);
   if (B * h * W > 0x7FFFFFFF || 9 * Cin > 0x7FFFFFFF) return fail(DP_ERR_UNSUPPORTED, "%s: dimension exceeds 2^31", name);
   dp::clear_error();
   GemmArgs g{};

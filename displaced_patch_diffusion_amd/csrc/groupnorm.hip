@@ -655,6 +655,7 @@ dp_status check_common(const char* name, const void* x, int64_t B, int64_t T_loc
   const int vec = dt == DP_BF16 ? 8 : 4;
   if (C % vec != 0 || C > 2048 || C / vec > kThreads || T_loc > 0x7FFFFFFF || B > 65535 || B * G > 0x7FFFFFFF)
     return fail(DP_ERR_UNSUPPORTED, "%s: C=%lld G=%lld not supported", name, (long long)C, (long long)G);
+  if (!dp::aligned16(x)) return fail(DP_ERR_INVALID_ARG, "%s: x must be 16-byte aligned", name);
   ga.x = x;
   ga.T = static_cast<int>(T_loc);
   ga.C = static_cast<int>(C);
@@ -774,6 +775,7 @@ DP_API dp_status dp_groupnorm_stale_stats(const void* x, const float* stale_sums
   if (!ws || ws_size < need) return fail(DP_ERR_INVALID_ARG, "%s: workspace %zu < %zu bytes", name, ws_size, need);
   const size_t xb = static_cast<size_t>(B * T_loc * C) * dp::dtype_size(dt);
   if (dp::overlaps(x, xb, y, xb)) return fail(DP_ERR_INVALID_ARG, "%s: x and y overlap", name);
+  if (!dp::aligned16(y)) return fail(DP_ERR_INVALID_ARG, "%s: y must be 16-byte aligned", name);
   set_stats(ga, stale_sums, n_patches, rank, T_total, gamma, beta, eps, fuse_silu);
   dp::clear_error();
   for (int64_t b0 = 0; b0 < B; b0 += kMaxChunk) {
@@ -854,6 +856,7 @@ DP_API dp_status dp_groupnorm_stale_stats_noalloc(const void* x, const float* st
   // first call's zero fill may be enqueued: a non-OK return enqueues nothing
   const size_t xb = static_cast<size_t>(B * T_loc * C) * dp::dtype_size(dt);
   if (dp::overlaps(x, xb, y, xb)) return fail(DP_ERR_INVALID_ARG, "%s: x and y overlap", name);
+  if (!dp::aligned16(y)) return fail(DP_ERR_INVALID_ARG, "%s: y must be 16-byte aligned", name);
   void* ws = nullptr;
   if ((st = device_scratch(name, stream, &ws)) != DP_OK) return st;
   return dp_groupnorm_stale_stats(x, stale_sums, n_patches, rank, T_total, gamma, beta, eps, fuse_silu, y,
@@ -893,6 +896,7 @@ DP_API dp_status dp_groupnorm_apply(const void* x, const float* local_sums, cons
   if ((st = check_stats_args(name, stale_sums, n_patches, rank, T_total, T_loc, eps)) != DP_OK) return st;
   const size_t xb = static_cast<size_t>(B * T_loc * C) * dp::dtype_size(dt);
   if (dp::overlaps(x, xb, y, xb)) return fail(DP_ERR_INVALID_ARG, "%s: x and y overlap", name);
+  if (!dp::aligned16(y)) return fail(DP_ERR_INVALID_ARG, "%s: y must be 16-byte aligned", name);
   set_stats(ga, stale_sums, n_patches, rank, T_total, gamma, beta, eps, fuse_silu);
   dp::clear_error();
   launch_apply(ga, 0, static_cast<int>(B), local_sums, nullptr, y, dt, stream);

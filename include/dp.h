@@ -20,6 +20,12 @@
  *    never allocates, frees or retains them.  Tensors are dense and
  *    contiguous in the stated layout.  Inputs and outputs must not overlap,
  *    except that dp_kv_buffer_splice updates its buffers in place.
+ *  - Activations, weights and outputs of the bf16 GEMM/conv, bf16 attention
+ *    and GroupNorm calls are moved in 16-byte pieces: their base pointers
+ *    must be 16-byte aligned (torch allocations are; a slice that starts at a
+ *    row boundary keeps it when a row is a multiple of 16 bytes), else
+ *    DP_ERR_INVALID_ARG.  Statistics, gamma/beta and biases need only their
+ *    element alignment.
  *  - `dt` is the storage type of every activation/weight tensor of a call.
  *    Statistics, GroupNorm gamma/beta and biases are always float32.
  *  - Calls are asynchronous: arguments are validated on the host first (a

@@ -302,3 +302,18 @@ def test_groupnorm_noalloc_validation(lib):
     # overlapping x and y: rejected before the first call's scratch set-up
     st, msg = call(y=A + 2)
     assert st == _lib.DP_ERR_INVALID_ARG and "overlap" in msg
+
+
+def test_misaligned_vector_tensors_are_rejected(lib):
+    """16-byte pieces: a bf16 tensor whose base is not 16-byte aligned is
+    rejected on the host (the addresses are far apart: no overlap)."""
+    st, msg = status_and_error(lib.dp_linear, A + 8, Bp, None, Cp, 64, 64, 64, _lib.DP_BF16, None)
+    assert st == _lib.DP_ERR_INVALID_ARG and "aligned" in msg
+    st, msg = status_and_error(lib.dp_linear, A, Bp, None, Cp + 2, 64, 64, 64, _lib.DP_BF16, None)
+    assert st == _lib.DP_ERR_INVALID_ARG and "aligned" in msg
+    st, msg = status_and_error(lib.dp_attn_stale_kv, A, Bp + 8, Cp, D, 1, 1, 64, 64, 64, 0.0, _lib.DP_BF16, E, 1 << 20,
+                               None)
+    assert st == _lib.DP_ERR_INVALID_ARG and "aligned" in msg
+    st, msg = status_and_error(lib.dp_groupnorm_apply, A + 4, Bp, None, 1, 0, 64, None, None, 1e-5, 0, Cp, 1, 64, 64,
+                               32, _lib.DP_BF16, None)
+    assert st == _lib.DP_ERR_INVALID_ARG and "aligned" in msg
