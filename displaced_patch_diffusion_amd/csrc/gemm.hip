@@ -439,7 +439,9 @@ __global__ void __launch_bounds__(64 * NW, OCC) gemm_bf16(GemmArgs g) {
   // which cost a third of a short-K projection.  Instead the tile (bias
   // added, rounded to bf16) goes to LDS (the ring is free once every wave is
   // past its last operand read), rows padded by 16 bytes, and leaves in
-  // 16-byte chunks, consecutive threads on consecutive chunks of a row.
+  // 16-byte chunks, consecutive threads on consecutive chunks of a row, by
+  // nontemporal stores (outputs of 18 MB and more do not stay in a 4 MB L2;
+  // the next op reads them from the last-level cache either way).
   constexpr int kTileStride = BN * 2 + 16;  // bytes per tile row
   // GroupNorm column sums: one thread per channel pair and row part
   constexpr int kPairs = BN / 2, kParts = (64 * NW) / kPairs > 0 ? (64 * NW) / kPairs : 1;
@@ -477,7 +479,8 @@ __global__ void __launch_bounds__(64 * NW, OCC) gemm_bf16(GemmArgs g) {
       const int seg = n / g.map.seg_n;  // 8 channels never straddle a segment (seg_n % 32 == 0)
       bf16_t* yrow = static_cast<bf16_t*>(g.map.outs[seg]) + out_row(g.map, seg, m) * g.map.seg_n -
                      seg * g.map.seg_n;
-      *reinterpret_cast<u32x4*>(yrow + n) = *reinterpret_cast<const u32x4*>(lds + r * kTileStride + c * 2);
+      __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(lds + r * kTileStride + c * 2),
+                                  reinterpret_cast<u32x4*>(yrow + n));
     }
   }
 
