@@ -35,8 +35,9 @@
  *  - State kept between calls, none of it caller data: the calling thread's
  *    last-error string; per device, a zero-filled 4 KiB device page the conv
  *    reads in place of absent halo rows and columns outside the image; per
- *    thread, each device's CU count and the attention kernels' resident
- *    blocks per CU, asked of the runtime once; per device, the 4 MiB scratch
+ *    thread, the current device's CU count (asked again when the thread
+ *    switches devices) and each device's resident attention blocks per CU
+ *    (asked once); per device, the 4 MiB scratch
  *    of dp_groupnorm_stale_stats_noalloc and its address.  The environment
  *    variable DP_ATTN_SCHEDULE is read at every attention call and query.
  *    Calls on one stream are ordered; concurrent calls on different streams
