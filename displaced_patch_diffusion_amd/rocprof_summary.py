@@ -52,6 +52,8 @@ PASSES = {
            "SQ_ACTIVE_INST_VALU", "SQ_WAIT_INST_LDS", "SQ_WAIT_ANY", "SQ_WAVE_CYCLES", "GRBM_GUI_ACTIVE"],
     "rd": ["TCC_EA0_RDREQ_32B_sum", "TCC_EA0_RDREQ_64B_sum", "TCC_EA0_RDREQ_128B_sum", "TCC_EA0_RDREQ_sum"],
     "wr": ["TCC_EA0_WRREQ_sum", "TCC_EA0_WRREQ_64B_sum", "TCC_EA0_RDREQ_DRAM_sum", "TCC_EA0_WRREQ_DRAM_sum"],
+    "lds": ["SQ_LDS_IDX_ACTIVE", "SQ_LDS_BANK_CONFLICT", "SQ_INSTS_LDS_LOAD_BANDWIDTH", "SQ_INSTS_LDS_STORE_BANDWIDTH",
+            "GRBM_GUI_ACTIVE"],
 }
 
 
@@ -210,6 +212,13 @@ def _derive(c: dict, n_calls: int) -> dict:
                         ("SQ_ACTIVE_INST_VALU", "valu_pct_of_wave")):
             if k in per:
                 out[name] = round(100 * per[k] / wc, 2)
+        if "SQ_LDS_IDX_ACTIVE" in per and cyc:
+            out["lds_active_pct"] = round(100 * per["SQ_LDS_IDX_ACTIVE"] / (cyc * N_CU), 2)
+        if "SQ_LDS_BANK_CONFLICT" in per and cyc:
+            out["lds_bank_conflict_pct"] = round(100 * per["SQ_LDS_BANK_CONFLICT"] / (cyc * N_CU), 2)
+    for k, name in (("SQ_INSTS_LDS_LOAD_BANDWIDTH", "lds_read_bytes"), ("SQ_INSTS_LDS_STORE_BANDWIDTH", "lds_write_bytes")):
+        if k in per:
+            out[name] = per[k] * 64
     if "SQ_INSTS_VALU_MFMA_MOPS_BF16" in per:
         out["mfma_bf16_flop"] = per["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512
     if "TCC_EA0_RDREQ_sum" in per:
@@ -233,13 +242,21 @@ def ops_counters(dirs: list[str], log: str, cmds: list[str], durations: str | No
     kernel time at the 2.4 GHz peak clock, the basis of the peak flop rate."""
     rec = _profile_line(log)
     reps, labels = rec["reps"], rec["labels"]
-    sums = {lab: collections.defaultdict(float) for lab in labels}
+    # per pass, each op's counters summed over its dispatches; a counter that
+    # more than one pass collected (the clock) is averaged over those passes
+    sums = {lab: {} for lab in labels}
+    seen = {lab: collections.Counter() for lab in labels}
     for d in dirs:
         seg = segments(_counter_dispatches(d), labels)
         for lab in labels:
+            acc = collections.defaultdict(float)
             for x in seg[lab]:
                 for k, v in x["c"].items():
-                    sums[lab][k] += v
+                    acc[k] += v
+            for k, v in acc.items():
+                n = seen[lab][k]
+                sums[lab][k] = (sums[lab].get(k, 0.0) * n + v) / (n + 1)
+                seen[lab][k] = n + 1
     res = {"workload": rec["workload"], "reps": reps, "sources_sha256": source_digest(), "ops": {}}
     dur = (read_result(durations) or {}).get("ops", {}) if durations else {}
     for lab in labels:
@@ -257,7 +274,9 @@ def ops_counters(dirs: list[str], log: str, cmds: list[str], durations: str | No
           "# valu_busy = SQ_ACTIVE_INST_VALU / (clock cycles x 256 CUs); waits as shares of SQ_WAVE_CYCLES",
           "# mfma bf16 flop = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512",
           "# read bytes = 32 x RDREQ_32B + 64 x RDREQ_64B + 128 x RDREQ_128B; write bytes = 64 x WRREQ_64B + "
-          "32 x (WRREQ - WRREQ_64B) (L2 <-> fabric; last-level cache hits included)"]
+          "32 x (WRREQ - WRREQ_64B) (L2 <-> fabric; last-level cache hits included)",
+          "# lds active / bank conflict = SQ_LDS_IDX_ACTIVE / SQ_LDS_BANK_CONFLICT over (clock cycles x 256 CUs); "
+          "LDS bytes = SQ_INSTS_LDS_{LOAD,STORE}_BANDWIDTH x 64; a counter two passes took is averaged"]
     if "read_bytes" in cal or "write_bytes" in cal:
         half = sb / 2
         L.append(f"# calibration: splice_copy reads {half:.0f} bytes and writes {half:.0f} bytes per call; "
@@ -269,7 +288,7 @@ def ops_counters(dirs: list[str], log: str, cmds: list[str], durations: str | No
         L.append(f"# mfma@2.4 = SQ_VALU_MFMA_BUSY_CYCLES / 1024 SIMDs / (traced us x 2400 MHz); traced durations "
                  f"from {os.path.basename(durations)}")
     L += ["#", f"# {'op':12s} {'mfma%':>7s} {'mfma@2.4':>8s} {'valu%':>7s} {'ldsw%':>7s} {'wait%':>7s} {'GFLOP':>9s} "
-               f"{'read MB':>9s} {'write MB':>9s} {'cycles':>9s}"]
+               f"{'read MB':>9s} {'write MB':>9s} {'cycles':>9s} {'lds%':>6s} {'ldsMB':>8s}"]
     for lab in labels:
         o = res["ops"][lab]
 
@@ -277,7 +296,8 @@ def ops_counters(dirs: list[str], log: str, cmds: list[str], durations: str | No
             return format(o[k] * scale, fmt) if k in o else " " * int(fmt.split(".")[0])
         L.append(f"  {lab:12s} {f('mfma_busy_pct')} {f('mfma_busy_pct_at_peak_clock', 1, '8.2f')} {f('valu_busy_pct')} {f('lds_wait_pct_of_wave')} "
                  f"{f('any_wait_pct_of_wave')} {f('mfma_bf16_flop', 1e-9, '9.2f')} {f('read_bytes', 1e-6, '9.2f')} "
-                 f"{f('write_bytes', 1e-6, '9.2f')} {f('gui_cycles', 1, '9.0f')}")
+                 f"{f('write_bytes', 1e-6, '9.2f')} {f('gui_cycles', 1, '9.0f')} {f('lds_active_pct', 1, '6.1f')} "
+                 f"{f('lds_read_bytes', 1e-6, '8.0f')}")
     L.append("RESULT " + json.dumps(res))
     return "\n".join(L) + "\n"
 

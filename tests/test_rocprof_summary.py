@@ -66,7 +66,8 @@ def test_ops_counters_bytes_and_busy(tmp_path):
         copy = name == "copy"
         # copy: 2000 bytes read per call as 10 x 32B + 5 x 64B + 10 x 128B (320+320+1280 = 1920) + 80 unclassified
         vals = {"TCC_EA0_RDREQ_32B_sum": 10 if copy else 1, "TCC_EA0_RDREQ_64B_sum": 5 if copy else 0,
-                "TCC_EA0_RDREQ_128B_sum": 10 if copy else 0, "TCC_EA0_RDREQ_sum": 25 if copy else 1}
+                "TCC_EA0_RDREQ_128B_sum": 10 if copy else 0, "TCC_EA0_RDREQ_sum": 25 if copy else 1,
+                "GRBM_GUI_ACTIVE": 8 * 1000}  # the clock in both passes: averaged, not added
         rows_rd += [{"Dispatch_Id": i + 1, "Kernel_Name": name, "Counter_Name": k, "Counter_Value": v}
                     for k, v in vals.items()]
         sq = {"GRBM_GUI_ACTIVE": 8 * 1000, "SQ_VALU_MFMA_BUSY_CYCLES": 1024 * 250 if name == "kc" else 0,
