@@ -64,7 +64,7 @@ def test_ops_counters_bytes_and_busy(tmp_path):
     rows_rd, rows_sq = [], []
     for i, (name, _) in enumerate(seq):
         copy = name == "copy"
-        # copy: 2000 bytes read per call as 10 x 32B + 5 x 64B + 10 x 128B (320+320+1280 = 1920) + 80 unclassified
+        # copy: 10 x 32B + 5 x 64B + 10 x 128B = 1920 bytes read per call, every request classified
         vals = {"TCC_EA0_RDREQ_32B_sum": 10 if copy else 1, "TCC_EA0_RDREQ_64B_sum": 5 if copy else 0,
                 "TCC_EA0_RDREQ_128B_sum": 10 if copy else 0, "TCC_EA0_RDREQ_sum": 25 if copy else 1,
                 "GRBM_GUI_ACTIVE": 8 * 1000}  # the clock in both passes: averaged, not added
