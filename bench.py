@@ -616,7 +616,8 @@ def splice_timing(torch, ops, share, K: int, reps: int, flush):
 def config_summary(torch, ops, synth, name: str, K: int, reps: int, flush):
     """Another workload's share: per-op numbers and the step's medians."""
     w = synth.WORKLOADS[name]
-    share = make_share(w)
+    # the conv epilogue forms GroupNorm sums in bf16 only
+    share = make_share(w, DEFAULT_QKV, DEFAULT_GN_SUMS if w.dtype == "bf16" else "separate")
     for _ in range(3):
         share.step(lambda n: None)
     torch.cuda.synchronize()
@@ -767,7 +768,7 @@ def main():
                          "pass; separate: the GroupNorm forms them in a read pass of its own")
     ap.add_argument("--no-otil", action="store_true", help="skip the OTIL selective-transmit timing")
     ap.add_argument("--no-vae", action="store_true", help="skip the row-sharded VAE decoder timing")
-    ap.add_argument("--no-configs", action="store_true", help="skip the other bf16 workloads' numbers")
+    ap.add_argument("--no-configs", action="store_true", help="skip the other workloads' numbers")
     ap.add_argument("--seed", type=int, default=0,
                     help="another family of seeded input streams (0: the one the tests use)")
     ap.add_argument("--noise", type=float, default=None, help="std of the stale-state noise (default: the workload's)")
@@ -804,6 +805,9 @@ def main():
         w = w.with_noise(args.noise)
     synth.set_stream_salt(args.seed)
     torch.cuda.set_device(0)
+    if w.dtype != "bf16" and args.gn_sums == "conv":
+        log("bench: the conv epilogue forms GroupNorm sums in bf16 only; using --gn-sums separate")
+        args.gn_sums = "separate"
     log(f"bench: workload {w.name}: building inputs")
     share = make_share(w, args.qkv, args.gn_sums)
     names = []
@@ -868,9 +872,10 @@ def main():
     b2b["attn"] = attn_t * 1e6  # the timed steps' own attention time
     kern = kernel_table(w, b2b, hot, cold)
     achieved = fl["attn"] / attn_t / 1e12
-    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak_mfma,
+    bf = w.dtype == "bf16"
+    roofline = {"bound": "mfma" if bf else "alu", "achieved": round(achieved, 2), "peak": peak_mfma,
                 "unit": "TFLOP/s", "frac": round(achieved / peak_mfma, 4),
-                "traffic": _traffic_from_profile(w), "kernel": "attn_bf16_d64",
+                "traffic": _traffic_from_profile(w), "kernel": "attn_bf16_d64" if bf else f"attn_f32<{w.head_dim}>",
                 "work_per_launch": f"{fl['attn'] / 1e9:.2f} GFLOP"}
     splice = splice_timing(torch, ops, share, K, R, flush) if w.dtype == "bf16" else None
     log("bench: the step as a HIP graph")
@@ -902,7 +907,7 @@ def main():
     del share
     torch.cuda.empty_cache()
     if not args.no_configs:
-        others = [n for n in synth.WORKLOAD_ORDER if n != w.name and synth.WORKLOADS[n].dtype == "bf16"]
+        others = [n for n in synth.WORKLOAD_ORDER if n != w.name]
         out["configs"] = {}
         for n in others:
             log(f"bench: workload {n}")
@@ -915,6 +920,7 @@ def main():
     if not args.no_cpu_baseline:
         log("bench: CPU baseline (oracle on a bounded sample)")
         out["cpu_baseline"] = cpu_baseline(w, synth, args.cpu_seconds)
+        out["cpu_baseline"]["gpu_over_cpu"] = round(value / out["cpu_baseline"]["value"], 1)
     out["provenance"] = provenance(torch)
     print(json.dumps(out), flush=True)
 
