@@ -270,6 +270,15 @@ class Share:
                     self.G, y=self.gc[0], fresh_sums_out=self.fresh[0], ws=self.gn_ws)))
         return L
 
+    def gn_moved_bytes(self) -> int:
+        """Bytes the step's GroupNorms move: read x and write y, plus one more
+        read of x for each GroupNorm that forms its own sums."""
+        w = self.w
+        one = w.B * w.conv_T * w.conv_C * w.elem_bytes
+        if w.two_level:  # the first GroupNorm always forms its own sums
+            return 3 * one + (2 if self.gn_sums_in_conv else 3) * one
+        return (2 if self.gn_sums_in_conv else 3) * one
+
     def outputs(self):
         """Tensors the step writes and no op reads before writing (the K/V
         buffers, updated in place, are left out)."""
@@ -580,7 +589,10 @@ def measure_ops(torch, share, K: int, reps: int, flush):
     return b2b, hot, cold
 
 
-def kernel_table(w, b2b, hot, cold):
+def kernel_table(w, b2b, hot, cold, moved=None):
+    """Per-op records; `moved` maps an op to the bytes its kernels move when
+    that differs from the algorithmic count (a GroupNorm that forms its own
+    sums reads x twice)."""
     fl, by = w.flops(), w.bytes()
     peak_mfma = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
     kern = {}
@@ -596,6 +608,8 @@ def kernel_table(w, b2b, hot, cold):
             a = by[name] / t / 1e3
             rec.update({"GB/s": round(a, 1), "frac": round(a / PEAK_HBM_GBPS, 4),
                         "frac_cold": None if c is None else round(by[name] / c / 1e3 / PEAK_HBM_GBPS, 4)})
+            if moved and name in moved and moved[name] != by[name]:
+                rec.update({"moved_bytes": moved[name], "moved_GB/s": round(moved[name] / t / 1e3, 1)})
         kern[name] = rec
     return kern
 
@@ -630,7 +644,7 @@ def config_summary(torch, ops, synth, name: str, K: int, reps: int, flush):
            "step_us_hot_median": round(step_hot, 2),
            "step_us_cold_median": None if step_cold is None else round(step_cold, 2),
            "TFLOP/s_hot": round(sum(fl.values()) / step_hot / 1e6, 1),
-           "kernels": kernel_table(w, b2b, hot, cold)}
+           "kernels": kernel_table(w, b2b, hot, cold, {"groupnorm": share.gn_moved_bytes()})}
     if w.dtype == "bf16":
         out["splice"] = splice_timing(torch, ops, share, K, reps, flush)
     out["graph"] = graph_timing(torch, share, K, reps, flush)
@@ -870,7 +884,7 @@ def main():
     value = work / step_s / 1e12
     peak_mfma = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
     b2b["attn"] = attn_t * 1e6  # the timed steps' own attention time
-    kern = kernel_table(w, b2b, hot, cold)
+    kern = kernel_table(w, b2b, hot, cold, {"groupnorm": share.gn_moved_bytes()})
     achieved = fl["attn"] / attn_t / 1e12
     bf = w.dtype == "bf16"
     roofline = {"bound": "mfma" if bf else "alu", "achieved": round(achieved, 2), "peak": peak_mfma,
