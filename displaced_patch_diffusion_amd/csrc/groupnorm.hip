@@ -36,7 +36,7 @@ namespace {
 
 constexpr int kThreads = 512;
 constexpr int kTargetBlocks = 512;  // sums pass: about two blocks per CU
-constexpr int kUnroll = 8;          // 16-byte loads in flight per thread
+constexpr int kUnroll = 8;          // 16-byte loads in flight per thread (the sums pass's remainder switch assumes 8)
 constexpr int kApplyPasses = 8;     // apply pass: token passes per thread
 constexpr int kTicketGroup = 16;    // blocks per first-level ticket counter
 constexpr int kCounterStride = 32;  // uints between counters (one 128-byte line each)
@@ -58,7 +58,6 @@ struct GnArgs {
   const float* beta;
   float* fresh;        // [B][G][2] second copy of the local sums, or NULL
   const float* given;  // [B][G][2] local sums the apply pass normalises with
-  float* coef;         // [Bc][2][C] per-channel (scale, shift) of the launch's batch items, or NULL
   int T, C, G, tiles, tile_tokens, n_patches, rank, B, silu, counter_stride;
   int b0;  // first batch item of the launch (blockIdx.y counts from it); B is the total
   float inv_count, eps;
@@ -105,15 +104,6 @@ __device__ __forceinline__ int64_t vec_byte(int b, int t, int vi, const GnArgs& 
   return ((static_cast<int64_t>(b) * a.T + t) * a.C) * (BF16 ? 2 : 4) + static_cast<int64_t>(vi) * 16;
 }
 
-// The 16-byte vector vi of token t, or zeros when `on` is false or t >= t_end.
-template <bool BF16>
-__device__ __forceinline__ u32x4 load_or_zero(const GnArgs& a, int b, int t, int t_end, int vi, bool on) {
-  u32x4 u = u32x4{0u, 0u, 0u, 0u};
-  if (on && t < t_end)
-    u = *reinterpret_cast<const u32x4*>(static_cast<const char*>(a.x) + vec_byte<BF16>(b, t, vi, a));
-  return u;
-}
-
 template <bool BF16>
 __device__ __forceinline__ void acc_vec(const u32x4& u, float* s1, float* s2) {
   constexpr int VEC = BF16 ? 8 : 4;
@@ -123,6 +113,29 @@ __device__ __forceinline__ void acc_vec(const u32x4& u, float* s1, float* s2) {
   for (int j = 0; j < VEC; ++j) {
     s1[j] += v[j];
     s2[j] = fmaf(v[j], v[j], s2[j]);
+  }
+}
+
+// Adds R block passes of the thread's channel vector vi, tokens t0, t0 + tpp,
+// ..., to s1/s2 (zeros when `on` is false).  The loads are unconditional (a
+// token at or past t_end re-reads token t_end - 1 and adds zeros), so they
+// all go out before the first add and each add waits only for its own load.
+template <bool BF16, int R>
+__device__ __forceinline__ void acc_passes(const GnArgs& a, int b, int t0, int tpp, int t_end, int vi, bool on,
+                                           float* s1, float* s2) {
+  u32x4 raw[R];
+#pragma unroll
+  for (int u = 0; u < R; ++u) {
+    const int t = min(t0 + u * tpp, t_end - 1);
+    raw[u] = *reinterpret_cast<const u32x4*>(static_cast<const char*>(a.x) + vec_byte<BF16>(b, t, vi, a));
+  }
+#pragma unroll
+  for (int u = 0; u < R; ++u) {
+    const bool ok = on && t0 + u * tpp < t_end;
+    u32x4 w;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) w[e] = ok ? raw[u][e] : 0u;
+    acc_vec<BF16>(w, s1, s2);
   }
 }
 
@@ -160,9 +173,33 @@ __device__ __forceinline__ int group_lanes(int G) {
   return 1 << (31 - __clz(l));  // a power of two
 }
 
-// Sum of v over `lanes` adjacent lanes (a power of two <= 64): a fixed xor
-// butterfly, so every lane ends with the same, order-fixed total.
+// Sum of v over `lanes` adjacent lanes (a power of two <= 64), the same
+// order-fixed total in every lane.  Up to 16 lanes by DPP within a row: swap
+// neighbours, then pairs, then mirror the half-rows and the row (each step
+// adds two equal-sized partial totals, so all lanes of a group agree); beyond
+// that by an xor butterfly through LDS permutes.  Every lane of the wave must
+// be active.
+__device__ __forceinline__ float dpp_add(float v, int ctrl_sel) {
+  int o = 0;
+  const int x = __float_as_int(v);
+  switch (ctrl_sel) {
+    case 0: o = __builtin_amdgcn_update_dpp(0, x, 0xB1, 0xF, 0xF, false); break;   // quad_perm [1,0,3,2]
+    case 1: o = __builtin_amdgcn_update_dpp(0, x, 0x4E, 0xF, 0xF, false); break;   // quad_perm [2,3,0,1]
+    case 2: o = __builtin_amdgcn_update_dpp(0, x, 0x141, 0xF, 0xF, false); break;  // row_half_mirror
+    default: o = __builtin_amdgcn_update_dpp(0, x, 0x140, 0xF, 0xF, false); break; // row_mirror
+  }
+  return v + __int_as_float(o);
+}
 __device__ __forceinline__ float2 lane_sum(float2 v, int lanes) {
+  if (lanes <= 16) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      if ((2 << k) > lanes) break;
+      v.x = dpp_add(v.x, k);
+      v.y = dpp_add(v.y, k);
+    }
+    return v;
+  }
   for (int off = 1; off < lanes; off <<= 1) {
     v.x += __shfl_xor(v.x, off, 64);
     v.y += __shfl_xor(v.y, off, 64);
@@ -171,49 +208,81 @@ __device__ __forceinline__ float2 lane_sum(float2 v, int lanes) {
 }
 
 // Block-wide per-group sums of the per-thread channel sums s1/s2 (thread =
-// token lane tl x channel vector vi), in a fixed order: lds_r holds
-// [2][tpp*C] floats; thread (g, j) of the group's `lanes` adds the entries
-// j, j + lanes, ... of the group's (token lane, channel) entries, eight LDS
-// reads in flight at a time, then the lanes are combined by lane_sum.  The
-// result lands in gsum[G].  Starts and ends with a barrier.
+// token lane tl x channel vector vi), in a fixed order and in two steps: the
+// threads' sums go to lds_r as [2][tpp][C]; thread c adds channel c over the
+// token lanes, in lane order, into chan[c]; then one thread per group adds
+// the group's channel sums in order (groups of more than 32 channels: 16
+// lanes take channels j, j + 16, ... and are combined by lane_sum).  Every LDS
+// access of the first two steps is unit-stride across threads.  The result
+// lands in gsum[G].  Starts and ends with a barrier.
 template <int VEC>
 __device__ void block_group_sums(const float* s1, const float* s2, bool active, int tl, int vi,
-                                 int tpp, int C, int G, float* lds_r, float2* gsum) {
+                                 int tpp, int C, int G, float* lds_r, float2* chan, float2* gsum) {
   __syncthreads();
   if (active) {
+    f32x4* r1 = reinterpret_cast<f32x4*>(lds_r + tl * C + vi * VEC);
+    f32x4* r2 = reinterpret_cast<f32x4*>(lds_r + (tpp + tl) * C + vi * VEC);
 #pragma unroll
-    for (int j = 0; j < VEC; ++j) {
-      lds_r[tl * C + vi * VEC + j] = s1[j];
-      lds_r[tpp * C + tl * C + vi * VEC + j] = s2[j];
+    for (int j = 0; j < VEC / 4; ++j) {
+      r1[j] = f32x4{s1[4 * j], s1[4 * j + 1], s1[4 * j + 2], s1[4 * j + 3]};
+      r2[j] = f32x4{s2[4 * j], s2[4 * j + 1], s2[4 * j + 2], s2[4 * j + 3]};
     }
   }
   __syncthreads();
-  const int lanes = group_lanes(G), Cg = C / G, n = tpp * Cg;
   constexpr int U = 8;
-  for (int f = threadIdx.x; f < ((G * lanes + 63) / 64) * 64; f += kThreads) {
-    const int g = f / lanes, j = f % lanes;
+  for (int c = threadIdx.x; c < C; c += kThreads) {
     float2 acc = make_float2(0.f, 0.f);
-    if (g < G) {
-      for (int e0 = j; e0 < n; e0 += U * lanes) {
-        float v1[U], v2[U];
+    for (int t0 = 0; t0 < tpp; t0 += U) {
+      float v1[U], v2[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const int e = min(e0 + u * lanes, n - 1);
-          const int idx = (e / Cg) * C + g * Cg + e % Cg;
-          v1[u] = lds_r[idx];
-          v2[u] = lds_r[tpp * C + idx];
-        }
+      for (int u = 0; u < U; ++u) {
+        const int t = min(t0 + u, tpp - 1);
+        v1[u] = lds_r[t * C + c];
+        v2[u] = lds_r[(tpp + t) * C + c];
+      }
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-          if (e0 + u * lanes < n) {
-            acc.x += v1[u];
-            acc.y += v2[u];
-          }
+      for (int u = 0; u < U; ++u) {
+        if (t0 + u < tpp) {
+          acc.x += v1[u];
+          acc.y += v2[u];
         }
       }
     }
-    acc = lane_sum(acc, lanes);
-    if (g < G && j == 0) gsum[g] = acc;
+    chan[c] = acc;
+  }
+  __syncthreads();
+  const int Cg = C / G;
+  if (Cg <= 32) {  // one thread per group, its channels in order
+    for (int g = threadIdx.x; g < G; g += kThreads) {
+      float2 acc = make_float2(0.f, 0.f);
+      for (int e0 = 0; e0 < Cg; e0 += U) {
+        float2 v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) v[u] = chan[g * Cg + min(e0 + u, Cg - 1)];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          if (e0 + u < Cg) {
+            acc.x += v[u].x;
+            acc.y += v[u].y;
+          }
+        }
+      }
+      gsum[g] = acc;
+    }
+  } else {  // 16 lanes per group: channels j, j + 16, ..., then lane_sum
+    for (int f = threadIdx.x; f < ((G * 16 + 63) / 64) * 64; f += kThreads) {
+      const int g = f >> 4, j = f & 15;
+      float2 acc = make_float2(0.f, 0.f);
+      if (g < G) {
+        for (int e = j; e < Cg; e += 16) {
+          const float2 v = chan[g * Cg + e];
+          acc.x += v.x;
+          acc.y += v.y;
+        }
+      }
+      acc = lane_sum(acc, 16);
+      if (g < G && j == 0) gsum[g] = acc;
+    }
   }
   __syncthreads();
 }
@@ -319,31 +388,6 @@ __device__ __forceinline__ float2 add_stale(const GnArgs& a, float2 loc, int gb,
   }
   return loc;
 }
-__device__ __forceinline__ float2 image_sums(const GnArgs& a, float2 loc, int gb, int g) {
-  return add_stale(a, loc, gb, g, 0);
-}
-
-// The first kStalePre patches' stale sums of group g, loaded ahead so that
-// their latency overlaps other loads; added in patch order by stale_prefix.
-constexpr int kStalePre = 8;
-__device__ __forceinline__ void prefetch_stale(const GnArgs& a, int gb, int g, float2* pre) {
-#pragma unroll
-  for (int j = 0; j < kStalePre; ++j) {
-    const float* st = a.stale + ((static_cast<int64_t>(min(j, a.n_patches - 1)) * a.B + gb) * a.G + g) * 2;
-    pre[j] = a.n_patches > 1 ? make_float2(st[0], st[1]) : make_float2(0.f, 0.f);
-  }
-}
-__device__ __forceinline__ float2 stale_prefix(const GnArgs& a, float2 f, const float2* pre) {
-#pragma unroll
-  for (int j = 0; j < kStalePre; ++j) {
-    if (j < a.n_patches && j != a.rank) {
-      f.x += pre[j].x;
-      f.y += pre[j].y;
-    }
-  }
-  return f;
-}
-
 // ------------------------------------------------------------ tickets
 // Counts block `tile` of batch item b in; true for exactly one block, the last
 // of the item's `tiles` to arrive.  First-level counters take kTicketGroup
@@ -368,8 +412,8 @@ __device__ bool take_ticket(const GnArgs& a, int b, int tile) {
 template <bool BF16>
 __global__ void __launch_bounds__(kThreads) gn_partial(GnArgs a) {
   constexpr int VEC = BF16 ? 8 : 4;
-  __shared__ float lds_r[2 * kThreads * VEC];
-  __shared__ float lds_c[2 * 2048];
+  __shared__ __attribute__((aligned(16))) float lds_r[2 * kThreads * VEC];
+  __shared__ __attribute__((aligned(16))) float lds_c[2 * 2048];
   __shared__ float2 gsum[2048];
   __shared__ int last;
   const int vpt = a.C / VEC, tpp = kThreads / vpt;
@@ -383,17 +427,25 @@ __global__ void __launch_bounds__(kThreads) gn_partial(GnArgs a) {
   float s1[VEC], s2[VEC];
 #pragma unroll
   for (int j = 0; j < VEC; ++j) s1[j] = s2[j] = 0.f;
-  for (int k0 = 0; k0 < npass; k0 += kUnroll) {
-    u32x4 raw[kUnroll];
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u)
-      raw[u] = load_or_zero<BF16>(a, b, t_begin + tl + (k0 + u) * tpp, t_end, vi,
-                                  active && k0 + u < npass);
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u)
-      if (k0 + u < npass) acc_vec<BF16>(raw[u], s1, s2);
+  // idle threads (tl >= tpp) read the last token lane's vectors, which that
+  // lane's wave reads anyway, and add zeros
+  const int tlr = min(tl, tpp - 1);
+  int k0 = 0;
+  for (; k0 + kUnroll <= npass; k0 += kUnroll)
+    acc_passes<BF16, kUnroll>(a, b, t_begin + tlr + k0 * tpp, tpp, t_end, vi, active, s1, s2);
+  const int t0 = t_begin + tlr + k0 * tpp;
+  static_assert(kUnroll == 8, "one case per remainder below");
+  switch (npass - k0) {  // the remaining passes, fewer than kUnroll
+    case 1: acc_passes<BF16, 1>(a, b, t0, tpp, t_end, vi, active, s1, s2); break;
+    case 2: acc_passes<BF16, 2>(a, b, t0, tpp, t_end, vi, active, s1, s2); break;
+    case 3: acc_passes<BF16, 3>(a, b, t0, tpp, t_end, vi, active, s1, s2); break;
+    case 4: acc_passes<BF16, 4>(a, b, t0, tpp, t_end, vi, active, s1, s2); break;
+    case 5: acc_passes<BF16, 5>(a, b, t0, tpp, t_end, vi, active, s1, s2); break;
+    case 6: acc_passes<BF16, 6>(a, b, t0, tpp, t_end, vi, active, s1, s2); break;
+    case 7: acc_passes<BF16, 7>(a, b, t0, tpp, t_end, vi, active, s1, s2); break;
+    default: break;
   }
-  block_group_sums<VEC>(s1, s2, active, tl, vi, tpp, a.C, a.G, lds_r, gsum);
+  block_group_sums<VEC>(s1, s2, active, tl, vi, tpp, a.C, a.G, lds_r, reinterpret_cast<float2*>(lds_c), gsum);
   for (int g = tid; g < a.G; g += kThreads)
     store_coherent(a.partial + (static_cast<int64_t>(b) * a.tiles + tile) * a.G + g, gsum[g]);
   // the block's partials are complete at the coherence point before its ticket
@@ -402,52 +454,15 @@ __global__ void __launch_bounds__(kThreads) gn_partial(GnArgs a) {
   if (tid == 0) last = take_ticket(a, b, tile);
   __syncthreads();
   if (!last) return;
-  // the coefficient table's inputs (the group's first stale sums, the
-  // channels' gamma/beta) go out together with the fold's loads
-  const int gb = a.b0 + b;
-  float2 pre[kStalePre];
-  constexpr int kCpt = 2048 / kThreads;  // channels per thread, C <= 2048
-  float gpre[kCpt], bpre[kCpt];
-  if (a.coef) {
-    if (tid < a.G) prefetch_stale(a, gb, tid, pre);
-#pragma unroll
-    for (int k = 0; k < kCpt; ++k) {
-      const int c = min(tid + k * kThreads, a.C - 1);
-      gpre[k] = a.gamma ? a.gamma[c] : 1.f;
-      bpre[k] = a.beta ? a.beta[c] : 0.f;
-    }
-  }
   fold_partials(a, b, gsum);
-  __syncthreads();
-  float2* ms = reinterpret_cast<float2*>(lds_c);  // [G] (mean, rstd)
   for (int g = tid; g < a.G; g += kThreads) {
-    const float f1 = gsum[g].x, f2 = gsum[g].y;
+    const float2 f = gsum[g];
     const int64_t o = (static_cast<int64_t>(b) * a.G + g) * 2;
-    if (a.sums) {
-      a.sums[o] = f1;
-      a.sums[o + 1] = f2;
-    }
+    a.sums[o] = f.x;
+    a.sums[o + 1] = f.y;
     if (a.fresh) {
-      a.fresh[o] = f1;
-      a.fresh[o + 1] = f2;
-    }
-    if (a.coef) {
-      float2 f = make_float2(f1, f2);
-      f = g == tid ? add_stale(a, stale_prefix(a, f, pre), gb, g, kStalePre) : image_sums(a, f, gb, g);
-      ms[g] = group_stats(f.x, f.y, a.inv_count, a.eps);
-    }
-  }
-  if (!a.coef) return;
-  __syncthreads();
-  const int Cg = a.C / a.G;
-  float* cf = a.coef + static_cast<int64_t>(b) * 2 * a.C;
-#pragma unroll
-  for (int k = 0; k < kCpt; ++k) {
-    const int c = tid + k * kThreads;
-    if (c < a.C) {
-      const float2 af = channel_affine(ms[c / Cg], gpre[k], bpre[k]);
-      cf[c] = af.x;
-      cf[a.C + c] = af.y;
+      a.fresh[o] = f.x;
+      a.fresh[o + 1] = f.y;
     }
   }
 }
@@ -478,57 +493,43 @@ __device__ __forceinline__ void apply_store(const GnArgs& a, const u32x4* raw, i
 }
 
 // The thread's tokens: n of them, starting at vector index `base` of x/y
-// (16-byte units), stride_vec apart.
+// (16-byte units), stride_vec apart.  Idle threads (false) get the last token
+// lane's slot with n = 0.
 template <bool BF16, int NT>
 __device__ __forceinline__ bool apply_slot(const GnArgs& a, int& vi, int64_t& base, int& stride_vec, int& n) {
   constexpr int VEC = BF16 ? 8 : 4;
   const int vpt = a.C / VEC, tpp = NT / vpt;
   const int tl = threadIdx.x / vpt;
   vi = threadIdx.x - tl * vpt;
-  if (tl >= tpp) return false;
-  const int t = blockIdx.x * a.tile_tokens + tl;
-  n = t < a.T ? min(kApplyPasses, (a.T - t + tpp - 1) / tpp) : 0;
-  base = (static_cast<int64_t>(blockIdx.y) * a.T + t) * vpt + vi;
+  const int t = blockIdx.x * a.tile_tokens + min(tl, tpp - 1);
+  n = t < a.T && tl < tpp ? min(kApplyPasses, (a.T - t + tpp - 1) / tpp) : 0;
+  base = (static_cast<int64_t>(blockIdx.y) * a.T + min(t, a.T - 1)) * vpt + vi;
   stride_vec = tpp * vpt;
-  return true;
+  return tl < tpp;
 }
 
-// Two-pass GroupNorm, second pass: the channel coefficients come from the
-// table the sums pass wrote.
-template <bool BF16, int NT, bool SILU>
-__global__ void __launch_bounds__(NT) gn_apply_table(GnArgs a) {
-  constexpr int VEC = BF16 ? 8 : 4;
-  int vi, stride_vec, n;
-  int64_t base;
-  if (!apply_slot<BF16, NT>(a, vi, base, stride_vec, n)) return;
-  u32x4 raw[kApplyPasses];
+// The thread's kApplyPasses x vectors, loaded unconditionally so that every
+// load is in flight before the first is used and each use waits only for its
+// own: passes from n on re-read pass n - 1 (pass 0 when n = 0, whose base
+// apply_slot clamps to the last token), and their stores are skipped.
+__device__ __forceinline__ void apply_loads(const GnArgs& a, int64_t base, int stride_vec, int n, u32x4* raw) {
   const u32x4* x = static_cast<const u32x4*>(a.x);
 #pragma unroll
-  for (int u = 0; u < kApplyPasses; ++u) raw[u] = u < n ? x[base + static_cast<int64_t>(u) * stride_vec] : u32x4{0u, 0u, 0u, 0u};
-  const float* cf = a.coef + static_cast<int64_t>(blockIdx.y) * 2 * a.C + vi * VEC;
-  float sc[VEC], sh[VEC];
-#pragma unroll
-  for (int j = 0; j < VEC; j += 4) {
-    const f32x4 s4 = *reinterpret_cast<const f32x4*>(cf + j), h4 = *reinterpret_cast<const f32x4*>(cf + a.C + j);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      sc[j + e] = s4[e];
-      sh[j + e] = h4[e];
-    }
-  }
-  apply_store<BF16, SILU>(a, raw, base, stride_vec, n, sc, sh);
+  for (int u = 0; u < kApplyPasses; ++u) raw[u] = x[base + static_cast<int64_t>(min(u, max(n - 1, 0))) * stride_vec];
 }
 
-// GroupNorm from given local sums: the block stages its batch item's local
-// sums and the other patches' stale sums in LDS (a few loads per thread,
-// issued before the x loads, so the barrier waits for them only); thread g
-// then derives group g's (mean, rstd) with the arithmetic the sums pass uses
-// for its table (local sums, then the patches in order: both entry points
-// give bit-identical outputs), and after a second barrier every thread reads
-// its channels' statistics.  Stale sums beyond kStaleLds entries are read
+// Apply pass, from local sums (the workspace's, after the sums pass, or the
+// caller's): the block stages its batch item's local sums and the other
+// patches' stale sums in LDS.  With REG (G and n_patches * G at most NT) each
+// thread loads one entry of each into registers before its x loads and
+// writes them to LDS after issuing those, so no wait for the small loads
+// holds up the x loads; otherwise a loop stages them first.  Thread g then
+// derives group g's (mean, rstd) from the local sums plus the patches' stale
+// sums in patch order, and after a second barrier every thread takes its
+// channels' (scale, shift).  Stale sums beyond kStaleLds entries are read
 // from memory by thread g instead.
 constexpr int kStaleLds = 1024;  // float2 entries: patches * G
-template <bool BF16, int NT, bool SILU>
+template <bool BF16, int NT, bool SILU, bool REG>
 __global__ void __launch_bounds__(NT) gn_apply_sums(GnArgs a) {
   constexpr int VEC = BF16 ? 8 : 4;
   __shared__ float2 st_lds[kStaleLds];  // [n_patches][G] stale sums
@@ -539,21 +540,32 @@ __global__ void __launch_bounds__(NT) gn_apply_sums(GnArgs a) {
   const int G = a.G, Cg = a.C / G, gb = a.b0 + blockIdx.y;
   const bool staged = a.n_patches * G <= kStaleLds;
   const float* loc = a.given + static_cast<int64_t>(blockIdx.y) * G * 2;
-  for (int f = threadIdx.x; f < G; f += NT) g_lds[f] = make_float2(loc[f * 2], loc[f * 2 + 1]);
-  if (staged && a.n_patches > 1) {
-    for (int f = threadIdx.x; f < a.n_patches * G; f += NT) {
-      const int p = f / G, g = f - p * G;
-      const float* st = a.stale + ((static_cast<int64_t>(p) * a.B + gb) * G + g) * 2;
-      st_lds[f] = make_float2(st[0], st[1]);
-    }
-  }
   float gm[VEC], bt[VEC];
-  if (on) load_affine<VEC>(a, vi, gm, bt);
   u32x4 raw[kApplyPasses];
-  const u32x4* x = static_cast<const u32x4*>(a.x);
-#pragma unroll
-  for (int u = 0; u < kApplyPasses; ++u)
-    raw[u] = on && u < n ? x[base + static_cast<int64_t>(u) * stride_vec] : u32x4{0u, 0u, 0u, 0u};
+  if constexpr (REG) {
+    // every thread loads (clamped indexes; the stale pointer falls back to
+    // the local sums when there are no other patches) and writes only its own
+    const int tid = threadIdx.x, fl = min(tid, G - 1);
+    const float2 lv = make_float2(loc[fl * 2], loc[fl * 2 + 1]);
+    const int fs = min(tid, a.n_patches * G - 1), sp = fs / G, sg = fs - sp * G;
+    const float* st = a.n_patches > 1 ? a.stale + ((static_cast<int64_t>(sp) * a.B + gb) * G + sg) * 2 : loc;
+    const float2 sv = make_float2(st[0], st[1]);
+    load_affine<VEC>(a, vi, gm, bt);
+    apply_loads(a, base, stride_vec, n, raw);
+    if (tid < G) g_lds[tid] = lv;
+    if (a.n_patches > 1 && tid < a.n_patches * G) st_lds[tid] = sv;
+  } else {
+    for (int f = threadIdx.x; f < G; f += NT) g_lds[f] = make_float2(loc[f * 2], loc[f * 2 + 1]);
+    if (staged && a.n_patches > 1) {
+      for (int f = threadIdx.x; f < a.n_patches * G; f += NT) {
+        const int p = f / G, g = f - p * G;
+        const float* st = a.stale + ((static_cast<int64_t>(p) * a.B + gb) * G + g) * 2;
+        st_lds[f] = make_float2(st[0], st[1]);
+      }
+    }
+    if (on) load_affine<VEC>(a, vi, gm, bt);
+    apply_loads(a, base, stride_vec, n, raw);
+  }
   __syncthreads();
   for (int g = threadIdx.x; g < G; g += NT) {
     float2 f = g_lds[g];
@@ -617,18 +629,18 @@ GnPlan apply_plan(int64_t T, int64_t C, dp_dtype dt) {
 // Workspace: the fixed counter region, then for one launch of up to
 // kMaxChunk batch items the folded sums and the tile partials.
 struct GnWs {
-  size_t sums_off, coef_off, partial_off, total;
+  size_t sums_off, partial_off, total;
   int counter_stride;  // uints per batch item
 };
 size_t round256(size_t n) { return (n + 255) / 256 * 256; }
 GnWs ws_layout(int64_t B, int64_t T, int64_t C, int64_t G) {
+  (void)C;
   const int64_t Bc = std::min<int64_t>(B, kMaxChunk);
   GnWs w{};
   const int64_t groups = (max_tiles(Bc, T) + kTicketGroup - 1) / kTicketGroup;
   w.counter_stride = static_cast<int>((1 + groups) * kCounterStride);
   w.sums_off = kCounterBytes;
-  w.coef_off = w.sums_off + round256(static_cast<size_t>(Bc) * G * 2 * sizeof(float));
-  w.partial_off = w.coef_off + round256(static_cast<size_t>(Bc) * C * 2 * sizeof(float));
+  w.partial_off = w.sums_off + round256(static_cast<size_t>(Bc) * G * 2 * sizeof(float));
   w.total = w.partial_off + static_cast<size_t>(Bc) * max_tiles(Bc, T) * G * sizeof(float2);
   return w;
 }
@@ -690,9 +702,8 @@ void set_stats(GnArgs& ga, const float* stale_sums, int64_t n_patches, int64_t r
 }
 
 // Sums pass over batch items [b0, b0 + Bc) of the call (Bc <= kMaxChunk):
-// local sums into the workspace (and `fresh`, already offset to b0) and,
-// when `table` is set, the apply pass's coefficient table.
-void launch_sums(GnArgs ga, int b0, int Bc, void* ws, float* fresh, bool table, dp_dtype dt, hipStream_t st) {
+// local sums into the workspace (and `fresh`, already offset to b0).
+void launch_sums(GnArgs ga, int b0, int Bc, void* ws, float* fresh, dp_dtype dt, hipStream_t st) {
   const GnWs w = ws_layout(Bc, ga.T, ga.C, ga.G);
   const GnPlan p = sums_plan(Bc, ga.T, ga.C, dt);
   char* base = static_cast<char*>(ws);
@@ -701,7 +712,6 @@ void launch_sums(GnArgs ga, int b0, int Bc, void* ws, float* fresh, bool table, 
   ga.counters = reinterpret_cast<unsigned*>(base);
   ga.counter_stride = w.counter_stride;
   ga.sums = reinterpret_cast<float*>(base + w.sums_off);
-  ga.coef = table ? reinterpret_cast<float*>(base + w.coef_off) : nullptr;
   ga.partial = reinterpret_cast<float2*>(base + w.partial_off);
   ga.fresh = fresh;
   ga.tiles = p.tiles;
@@ -711,43 +721,35 @@ void launch_sums(GnArgs ga, int b0, int Bc, void* ws, float* fresh, bool table, 
   else hipLaunchKernelGGL(gn_partial<false>, grid, dim3(kThreads), 0, st, ga);
 }
 
-// Apply pass over batch items [b0, b0 + Bc): from the coefficient table
-// `coef` ([Bc][2][C], written by the sums pass) when given, else from the
-// local sums `local_sums` ([Bc][G][2]) and the stale sums.
-void launch_apply(GnArgs ga, int b0, int Bc, const float* local_sums, float* coef, void* y, dp_dtype dt,
-                  hipStream_t st) {
+// Apply pass over batch items [b0, b0 + Bc) from their local sums
+// `local_sums` ([Bc][G][2]) and the stale sums.
+void launch_apply(GnArgs ga, int b0, int Bc, const float* local_sums, void* y, dp_dtype dt, hipStream_t st) {
   const GnPlan p = apply_plan(ga.T, ga.C, dt);
   const size_t off = static_cast<size_t>(b0) * ga.T * ga.C * dp::dtype_size(dt);
   ga.x = static_cast<const char*>(ga.x) + off;
   ga.y = static_cast<char*>(y) + off;
   ga.b0 = b0;
   ga.given = local_sums;
-  ga.coef = coef;
   ga.tiles = p.tiles;
   ga.tile_tokens = p.tile_tokens;
   const dim3 grid(static_cast<unsigned>(p.tiles), static_cast<unsigned>(Bc));
   const bool wide = apply_threads(ga.C, dt) == 512;
-  const int k = (coef ? 8 : 0) + (dt == DP_BF16 ? 4 : 0) + (wide ? 2 : 0) + (ga.silu ? 1 : 0);
+  const int nt = wide ? 512 : 256;
+  const bool reg = ga.G <= nt && static_cast<int64_t>(ga.n_patches) * ga.G <= nt;
+  const int k = (dt == DP_BF16 ? 8 : 0) + (wide ? 4 : 0) + (ga.silu ? 2 : 0) + (reg ? 1 : 0);
   switch (k) {
-#define DP_GN_APPLY(K, KERN, BF, NT, SI) \
-  case K: hipLaunchKernelGGL((KERN<BF, NT, SI>), grid, dim3(NT), 0, st, ga); break;
-    DP_GN_APPLY(0, gn_apply_sums, false, 256, false)
-    DP_GN_APPLY(1, gn_apply_sums, false, 256, true)
-    DP_GN_APPLY(2, gn_apply_sums, false, 512, false)
-    DP_GN_APPLY(3, gn_apply_sums, false, 512, true)
-    DP_GN_APPLY(4, gn_apply_sums, true, 256, false)
-    DP_GN_APPLY(5, gn_apply_sums, true, 256, true)
-    DP_GN_APPLY(6, gn_apply_sums, true, 512, false)
-    DP_GN_APPLY(7, gn_apply_sums, true, 512, true)
-    DP_GN_APPLY(8, gn_apply_table, false, 256, false)
-    DP_GN_APPLY(9, gn_apply_table, false, 256, true)
-    DP_GN_APPLY(10, gn_apply_table, false, 512, false)
-    DP_GN_APPLY(11, gn_apply_table, false, 512, true)
-    DP_GN_APPLY(12, gn_apply_table, true, 256, false)
-    DP_GN_APPLY(13, gn_apply_table, true, 256, true)
-    DP_GN_APPLY(14, gn_apply_table, true, 512, false)
-    DP_GN_APPLY(15, gn_apply_table, true, 512, true)
-#undef DP_GN_APPLY
+#define DP_GN_SUMS(K, BF, NT, SI) \
+  case 2 * K: hipLaunchKernelGGL((gn_apply_sums<BF, NT, SI, false>), grid, dim3(NT), 0, st, ga); break; \
+  case 2 * K + 1: hipLaunchKernelGGL((gn_apply_sums<BF, NT, SI, true>), grid, dim3(NT), 0, st, ga); break;
+    DP_GN_SUMS(0, false, 256, false)
+    DP_GN_SUMS(1, false, 256, true)
+    DP_GN_SUMS(2, false, 512, false)
+    DP_GN_SUMS(3, false, 512, true)
+    DP_GN_SUMS(4, true, 256, false)
+    DP_GN_SUMS(5, true, 256, true)
+    DP_GN_SUMS(6, true, 512, false)
+    DP_GN_SUMS(7, true, 512, true)
+#undef DP_GN_SUMS
   }
 }
 
@@ -780,10 +782,10 @@ DP_API dp_status dp_groupnorm_stale_stats(const void* x, const float* stale_sums
   dp::clear_error();
   for (int64_t b0 = 0; b0 < B; b0 += kMaxChunk) {
     const int Bc = static_cast<int>(std::min<int64_t>(kMaxChunk, B - b0));
-    launch_sums(ga, static_cast<int>(b0), Bc, ws, fresh_sums_out ? fresh_sums_out + b0 * G * 2 : nullptr, true, dt,
-                stream);
-    launch_apply(ga, static_cast<int>(b0), Bc, nullptr,
-                 reinterpret_cast<float*>(static_cast<char*>(ws) + ws_layout(Bc, T_loc, C, G).coef_off), y, dt, stream);
+    launch_sums(ga, static_cast<int>(b0), Bc, ws, fresh_sums_out ? fresh_sums_out + b0 * G * 2 : nullptr, dt, stream);
+    launch_apply(ga, static_cast<int>(b0), Bc,
+                 reinterpret_cast<const float*>(static_cast<char*>(ws) + ws_layout(Bc, T_loc, C, G).sums_off), y, dt,
+                 stream);
   }
   return dp::check_launch(name);
 }
@@ -879,7 +881,7 @@ DP_API dp_status dp_groupnorm_sums(const void* x, float* sums_out, int64_t B, in
   dp::clear_error();
   for (int64_t b0 = 0; b0 < B; b0 += kMaxChunk)
     launch_sums(ga, static_cast<int>(b0), static_cast<int>(std::min<int64_t>(kMaxChunk, B - b0)), ws,
-                sums_out + b0 * G * 2, false, dt, stream);
+                sums_out + b0 * G * 2, dt, stream);
   return dp::check_launch(name);
 }
 
@@ -899,6 +901,6 @@ DP_API dp_status dp_groupnorm_apply(const void* x, const float* local_sums, cons
   if (!dp::aligned16(y)) return fail(DP_ERR_INVALID_ARG, "%s: y must be 16-byte aligned", name);
   set_stats(ga, stale_sums, n_patches, rank, T_total, gamma, beta, eps, fuse_silu);
   dp::clear_error();
-  launch_apply(ga, 0, static_cast<int>(B), local_sums, nullptr, y, dt, stream);
+  launch_apply(ga, 0, static_cast<int>(B), local_sums, y, dt, stream);
   return dp::check_launch(name);
 }
