@@ -72,33 +72,10 @@ struct GemmArgs {
   int tiles_m, tiles_n, units, units_per_xcd;
   // conv with GroupNorm sums only:
   float2* gpart;       // per (tile row, batch segment, tile column, group slot) partials
-  unsigned* counters;  // ticket counters per batch item, kCounterStride apart
   float* gsums;        // [B][G][2] output
   int gT;              // output tokens per batch item
-  int G, Cg, slots, counter_stride;
-  int ticket;          // 1: the last tile of each batch item folds its sums; 0: a fold launch follows
+  int G, Cg, slots;
 };
-
-constexpr int kTicketGroup = 16;    // tiles per first-level ticket counter
-constexpr int kCounterStride = 32;  // uints between counters (one 128-byte line each)
-// Ticket counters live in a fixed region at the start of the workspace, the
-// same for every shape, and nothing else is ever written there: a workspace
-// zero-filled once stays valid for any sequence of calls.
-constexpr int kCounterBytes = 32768;
-// The last tile folds its batch item's partials only up to this many bytes of
-// them (a one-block fold); larger folds run as their own launch.
-constexpr int kTicketFoldBytes = 65536;
-
-// Device-coherent 8-byte store and load (agent scope: they bypass the per-XCD
-// L2, so blocks on other XCDs see them within the same launch).
-__device__ __forceinline__ void store_coherent(float2* p, float2 v) {
-  __hip_atomic_store(reinterpret_cast<unsigned long long*>(p), __builtin_bit_cast(unsigned long long, v),
-                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float2 load_coherent(const float2* p) {
-  return __builtin_bit_cast(float2, __hip_atomic_load(reinterpret_cast<const unsigned long long*>(p),
-                                                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-}
 
 // Sum of v over `lanes` adjacent lanes (a power of two <= 64) by a fixed xor
 // butterfly: every lane ends with the same, order-fixed total.
@@ -119,62 +96,6 @@ __device__ __forceinline__ int pow2_lanes(int n) {
 __device__ __forceinline__ int2 batch_tile_rows(int b, int gT, int BM) {
   return make_int2(static_cast<int>((static_cast<int64_t>(b) * gT) / BM),
                    static_cast<int>(((static_cast<int64_t>(b) + 1) * gT - 1) / BM));
-}
-
-// Partial of group gi from the tile (tr, tc) for batch item b: the slot the
-// tile stored for that group.
-__device__ __forceinline__ const float2* gn_slot(const GemmArgs& g, int b, int gi, int tr, int tc, int BM, int BN) {
-  const int sgt = b - static_cast<int>((static_cast<int64_t>(tr) * BM) / g.gT);
-  return g.gpart + ((static_cast<int64_t>(tr) * 2 + sgt) * g.tiles_n + tc) * g.slots + gi - (tc * BN) / g.Cg;
-}
-
-// Sum over the partials of group gi for batch item b that lane q of `lanes`
-// owns: the (tile row, tile column) pairs e = q, q + lanes, ... in order,
-// eight loads in flight at a time.  COH selects device-coherent loads (inside
-// the launch that wrote them).
-template <bool COH>
-__device__ float2 fold_group_lane(const GemmArgs& g, int b, int gi, int q, int lanes, int BM, int BN) {
-  const int2 r = batch_tile_rows(b, g.gT, BM);
-  const int tn_lo = (gi * g.Cg) / BN, ntn = ((gi + 1) * g.Cg - 1) / BN - tn_lo + 1;
-  const int total = (r.y - r.x + 1) * ntn;
-  constexpr int U = 8;
-  float2 s = make_float2(0.f, 0.f);
-  for (int e0 = q; e0 < total; e0 += U * lanes) {
-    float2 v[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int e = min(e0 + u * lanes, total - 1);
-      const float2* p = gn_slot(g, b, gi, r.x + e / ntn, tn_lo + e % ntn, BM, BN);
-      v[u] = COH ? load_coherent(p) : *p;
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      if (e0 + u * lanes < total) {
-        s.x += v[u].x;
-        s.y += v[u].y;
-      }
-    }
-  }
-  return s;
-}
-
-// Counts tile (tm, tn) in for batch item b; true for exactly one tile, the last
-// of the item's tiles to arrive (two-level: kTicketGroup tiles per first-level
-// counter).  Every counter is back at zero once all tiles have arrived.
-__device__ bool take_batch_ticket(const GemmArgs& g, int b, int tm, int tn, int BM) {
-  const int2 r = batch_tile_rows(b, g.gT, BM);
-  const int n_tiles = (r.y - r.x + 1) * g.tiles_n;
-  const int idx = (tm - r.x) * g.tiles_n + tn;
-  const int grp = idx / kTicketGroup;
-  const unsigned in_grp = static_cast<unsigned>(min(kTicketGroup, n_tiles - grp * kTicketGroup));
-  const unsigned n_grp = static_cast<unsigned>((n_tiles + kTicketGroup - 1) / kTicketGroup);
-  unsigned* base = g.counters + static_cast<int64_t>(b) * g.counter_stride;
-  unsigned* gc = base + (1 + grp) * kCounterStride;
-  if (__hip_atomic_fetch_add(gc, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != in_grp - 1) return false;
-  __hip_atomic_store(gc, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  if (__hip_atomic_fetch_add(base, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != n_grp - 1) return false;
-  __hip_atomic_store(base, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  return true;
 }
 
 // LDS rows of 64 bytes (BK = 32) or 128 bytes (BK = 64): 16-byte chunk c of
@@ -490,9 +411,8 @@ __global__ void __launch_bounds__(64 * NW, OCC) gemm_bf16(GemmArgs g) {
     // gT >= BM).  Per channel pair and row part, one thread sums its rows of
     // each segment in row order; the parts are then added in part order, the
     // block sums the channels of each group its columns touch, in a fixed
-    // order, and stores one partial per (batch segment, group slot).  The
-    // last tile of a batch item to finish folds that item's partials into
-    // gsums.
+    // order, and stores one partial per (batch segment, group slot); the
+    // fold launch that follows adds them into gsums.
     float2* chan = reinterpret_cast<float2*>(lds + BM * kTileStride);  // [2][BN]
     float2* parts = chan + 2 * BN;                                     // [kParts][2][BN]
     const int b0 = m0 / g.gT;
@@ -556,86 +476,87 @@ __global__ void __launch_bounds__(64 * NW, OCC) gemm_bf16(GemmArgs g) {
         acc2 = lane_sum(acc2, sl);
         if (st < nseg * nslots && l == 0) {
           const int sg = st / nslots, jj = st - sg * nslots;
-          store_coherent(g.gpart + ((static_cast<int64_t>(tm) * 2 + sg) * g.tiles_n + tn) * g.slots + jj, acc2);
-        }
-      }
-    }
-    if (!g.ticket) return;
-    // the block's partials are complete at the coherence point before its tickets
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    __shared__ int fold_mask;
-    if (tid == 0) {
-      int mask = 0;
-      for (int sg = 0; sg < nseg; ++sg)
-        if (take_batch_ticket(g, b0 + sg, tm, tn, BM)) mask |= 1 << sg;
-      fold_mask = mask;
-    }
-    __syncthreads();
-    const int mask = fold_mask;
-    for (int sg = 0; sg < nseg; ++sg) {
-      if (!(mask & (1 << sg))) continue;
-      // Fold batch item b.  Its partials are one run of tiles_n * slots per
-      // tile row (the row's segment holding b): loaded all at once, coalesced,
-      // into LDS (the ring, free now); then lanes of each group add the
-      // group's slots from LDS, tile rows in order, then tile columns, and a
-      // lane tree combines them.
-      const int b = b0 + sg;
-      const int2 r = batch_tile_rows(b, g.gT, BM);
-      const int run = g.tiles_n * g.slots, total = (r.y - r.x + 1) * run;
-      float2* part = reinterpret_cast<float2*>(lds);  // [rows][tiles_n][slots]
-      __syncthreads();
-      constexpr int U = 8;
-      for (int e0 = tid; e0 < total; e0 += U * 64 * NW) {
-        float2 v[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const int e = min(e0 + u * 64 * NW, total - 1), rr = e / run;
-          const int sgt = b - static_cast<int>((static_cast<int64_t>(r.x + rr) * BM) / g.gT);
-          v[u] = load_coherent(g.gpart + (static_cast<int64_t>(r.x + rr) * 2 + sgt) * run + (e - rr * run));
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-          if (e0 + u * 64 * NW < total) part[e0 + u * 64 * NW] = v[u];
-      }
-      __syncthreads();
-      const int lanes = pow2_lanes((64 * NW) / g.G);
-      for (int f = tid; f < ((g.G * lanes + 63) / 64) * 64; f += 64 * NW) {
-        const int gi = f / lanes, q = f % lanes;
-        float2 sum = make_float2(0.f, 0.f);
-        if (gi < g.G) {
-          const int tn_lo = (gi * g.Cg) / BN, ntn = ((gi + 1) * g.Cg - 1) / BN - tn_lo + 1;
-          for (int rr = q; rr <= r.y - r.x; rr += lanes)
-            for (int c = 0; c < ntn; ++c) {
-              const float2 v = part[rr * run + (tn_lo + c) * g.slots + gi - ((tn_lo + c) * BN) / g.Cg];
-              sum.x += v.x;
-              sum.y += v.y;
-            }
-        }
-        sum = lane_sum(sum, lanes);
-        if (gi < g.G && q == 0) {
-          g.gsums[(static_cast<int64_t>(b) * g.G + gi) * 2] = sum.x;
-          g.gsums[(static_cast<int64_t>(b) * g.G + gi) * 2 + 1] = sum.y;
+          g.gpart[((static_cast<int64_t>(tm) * 2 + sg) * g.tiles_n + tn) * g.slots + jj] = acc2;
         }
       }
     }
   }
 }
 
-// The fold as a launch of its own (one block per (group, batch item)), for
-// convs whose partials are too many for one block: 256 lanes, added in order.
+// The fold of the conv's tile partials into gsums, a launch of its own after
+// the conv: one block per (group, batch item).  The group's partials are the
+// slot it owns in each (tile row, tile column) of the item's tile rows and the
+// group's tile columns; lane q takes entries q, q + 256, ... in (tile row,
+// tile column) order (eight loads in flight per pass when there are more
+// entries than lanes), then each wave adds its lanes by DPP steps within
+// 16-lane rows and its four row totals in order, and thread 0 the four waves
+// in order: one fixed order for a given shape.
 constexpr int kFoldThreads = 256;
+
+// The partial of entry e (tile row r0 + e / ntn, tile column tn_lo + e % ntn)
+// of group gi for batch item b; slot0 is gi's slot index in column tn_lo.
+template <int BM, int BN>
+__device__ __forceinline__ float2 fold_entry(const GemmArgs& g, int e, int r0, int tn_lo, int ntn, int gi,
+                                             int slot0, int64_t first_row) {
+  const int rr = ntn == 1 ? e : e / ntn, c = e - rr * ntn;
+  const int tr = r0 + rr, tc = tn_lo + c;
+  // a tile row that starts in batch item b - 1 holds b in its segment 1
+  const int sgt = static_cast<int64_t>(tr) * BM < first_row ? 1 : 0;
+  const int slot = c == 0 ? slot0 : gi - (tc * BN) / g.Cg;
+  return g.gpart[((static_cast<int64_t>(tr) * 2 + sgt) * g.tiles_n + tc) * g.slots + slot];
+}
+
+// Sum over the 64 lanes of a wave (lane 0 returns it): DPP steps inside each
+// 16-lane row (every lane then holds its row's total), then rows 0..3 in order.
+__device__ __forceinline__ float wave_sum(float v) {
+  const int x0 = __float_as_int(v);
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, x0, 0xB1, 0xF, 0xF, false));  // quad_perm [1,0,3,2]
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));  // [2,3,0,1]
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false));  // half mirror
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false));  // row mirror
+  const int xi = __float_as_int(v);
+  return ((__int_as_float(__builtin_amdgcn_readlane(xi, 0)) + __int_as_float(__builtin_amdgcn_readlane(xi, 16))) +
+          __int_as_float(__builtin_amdgcn_readlane(xi, 32))) +
+         __int_as_float(__builtin_amdgcn_readlane(xi, 48));
+}
+
 template <int BM, int BN>
 __global__ void __launch_bounds__(kFoldThreads) gn_conv_fold(GemmArgs g) {
-  __shared__ float2 red[kFoldThreads];
-  const int gi = blockIdx.x, b = blockIdx.y;
-  red[threadIdx.x] = fold_group_lane<false>(g, b, gi, threadIdx.x, kFoldThreads, BM, BN);
+  __shared__ float2 red[kFoldThreads / 64];
+  const int gi = blockIdx.x, b = blockIdx.y, q = threadIdx.x;
+  const int2 r = batch_tile_rows(b, g.gT, BM);
+  const int tn_lo = (gi * g.Cg) / BN, ntn = ((gi + 1) * g.Cg - 1) / BN - tn_lo + 1;
+  const int total = (r.y - r.x + 1) * ntn;
+  const int slot0 = gi - (tn_lo * BN) / g.Cg;
+  const int64_t first_row = static_cast<int64_t>(b) * g.gT;  // b's first output row
+  float2 s = make_float2(0.f, 0.f);
+  if (total <= kFoldThreads) {  // one entry per lane at most
+    if (q < total) s = fold_entry<BM, BN>(g, q, r.x, tn_lo, ntn, gi, slot0, first_row);
+  } else {
+    constexpr int U = 8;
+    for (int e0 = q; e0 < total; e0 += U * kFoldThreads) {
+      float2 v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        v[u] = fold_entry<BM, BN>(g, min(e0 + u * kFoldThreads, total - 1), r.x, tn_lo, ntn, gi, slot0, first_row);
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (e0 + u * kFoldThreads < total) {
+          s.x += v[u].x;
+          s.y += v[u].y;
+        }
+      }
+    }
+  }
+  const float sx = wave_sum(s.x), sy = wave_sum(s.y);
+  if ((q & 63) == 0) red[q >> 6] = make_float2(sx, sy);
   __syncthreads();
-  if (threadIdx.x == 0) {
+  if (q == 0) {
     float2 sum = red[0];
-    for (int q = 1; q < kFoldThreads; ++q) {
-      sum.x += red[q].x;
-      sum.y += red[q].y;
+#pragma unroll
+    for (int w = 1; w < kFoldThreads / 64; ++w) {
+      sum.x += red[w].x;
+      sum.y += red[w].y;
     }
     g.gsums[(static_cast<int64_t>(b) * g.G + gi) * 2] = sum.x;
     g.gsums[(static_cast<int64_t>(b) * g.G + gi) * 2 + 1] = sum.y;
@@ -688,9 +609,8 @@ void launch_bf16(const GemmArgs& base, hipStream_t st) {
     hipLaunchKernelGGL((gemm_bf16<t.bm, t.bn, t.wgm, t.nw, kBK, kStages, t.occ, CONV>), grid, dim3(64 * t.nw), 0, st, g);
 }
 
-// Conv with GroupNorm sums: same tile choice, GNS epilogue; the last tile of
-// each batch item folds its sums when the counters fit the fixed region and
-// the item's partials fit one block's fold, else a fold launch follows.
+// Conv with GroupNorm sums: same tile choice, GNS epilogue, then the fold
+// launch.
 template <int C>
 void launch_bf16_gns(const GemmArgs& base, hipStream_t st) {
   constexpr TileCfg t = kTiles[C];
@@ -700,22 +620,14 @@ void launch_bf16_gns(const GemmArgs& base, hipStream_t st) {
   g.units = g.tiles_m * g.tiles_n;
   g.units_per_xcd = (g.units + kXcds - 1) / kXcds;
   g.slots = (t.bn + g.Cg - 1) / g.Cg + 1;
-  const int64_t tiles_b = ((static_cast<int64_t>(g.gT) + t.bm - 1) / t.bm + 1) * g.tiles_n;
   const int64_t B = g.M / g.gT;
-  g.counter_stride = static_cast<int>((1 + (tiles_b + kTicketGroup - 1) / kTicketGroup) * kCounterStride);
-  // the last tile stages its batch item's partials in the LDS ring
-  const int64_t ring = g.K % t.bk == 0 ? static_cast<int64_t>(t.st) * (t.bm + t.bn) * 2 * t.bk
-                                       : static_cast<int64_t>(kStages) * (t.bm + t.bn) * 2 * kBK;
-  g.ticket = B * g.counter_stride * 4 <= kCounterBytes &&
-             tiles_b * g.slots * static_cast<int64_t>(sizeof(float2)) <= std::min<int64_t>(ring, kTicketFoldBytes);
   const dim3 grid(static_cast<unsigned>(g.units_per_xcd * kXcds));
   if (g.K % t.bk == 0)
     hipLaunchKernelGGL((gemm_bf16<t.bm, t.bn, t.wgm, t.nw, t.bk, t.st, t.occ, true, true>), grid, dim3(64 * t.nw), 0, st, g);
   else
     hipLaunchKernelGGL((gemm_bf16<t.bm, t.bn, t.wgm, t.nw, kBK, kStages, t.occ, true, true>), grid, dim3(64 * t.nw), 0, st, g);
-  if (!g.ticket)
-    hipLaunchKernelGGL((gn_conv_fold<t.bm, t.bn>), dim3(static_cast<unsigned>(g.G), static_cast<unsigned>(B)),
-                       dim3(kFoldThreads), 0, st, g);
+  hipLaunchKernelGGL((gn_conv_fold<t.bm, t.bn>), dim3(static_cast<unsigned>(g.G), static_cast<unsigned>(B)),
+                     dim3(kFoldThreads), 0, st, g);
 }
 
 // Tile shape: fewest tiles per CU times tile area times the shape's cost per
@@ -962,9 +874,10 @@ DP_API dp_status dp_qkv_projection_into_buffers(const void* x, const void* wq, c
 }
 
 namespace {
-// Workspace of the conv with GroupNorm sums: the fixed counter region, then the
-// (tile row, batch segment, tile column, group slot) partials, sized for every
-// tile shape the planner may pick and for one channel per group.
+// Workspace of the conv with GroupNorm sums: the (tile row, batch segment,
+// tile column, group slot) partials, sized for every tile shape the planner
+// may pick and for one channel per group.  Every slot the fold reads is
+// written by the same call, so the workspace needs no initial contents.
 struct ConvGnWs {
   size_t partial_off, total;
 };
@@ -976,7 +889,7 @@ ConvGnWs conv_gn_ws(int64_t B, int64_t h, int64_t W, int64_t Cout) {
     part = std::max(part, tm * 2 * tn * (t.bn + 1));
   }
   ConvGnWs w{};
-  w.partial_off = kCounterBytes;
+  w.partial_off = 0;
   w.total = w.partial_off + static_cast<size_t>(part) * sizeof(float2);
   return w;
 }
@@ -1029,7 +942,6 @@ DP_API dp_status dp_conv3x3_stale_halo_gn_sums(const void* x, const void* halo_t
   g.N = (int)Cout;
   g.K = (int)(9 * Cin);
   const ConvGnWs lay = conv_gn_ws(B, h, W, Cout);
-  g.counters = static_cast<unsigned*>(ws);
   g.gpart = reinterpret_cast<float2*>(static_cast<char*>(ws) + lay.partial_off);
   g.gsums = gn_sums;
   g.gT = (int)(h * W);

@@ -41,8 +41,8 @@ def _stream() -> int:
 
 
 def _ws(nbytes: int, device) -> torch.Tensor | None:
-    # zero-filled: the GroupNorm and conv-sums workspaces hold ticket counters
-    # that must start at zero (every call leaves them at zero again)
+    # zero-filled: the GroupNorm workspaces hold ticket counters that must
+    # start at zero (every call leaves them at zero again)
     return torch.zeros(nbytes, dtype=torch.uint8, device=device) if nbytes else None
 
 

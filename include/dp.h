@@ -148,14 +148,13 @@ dp_status dp_conv3x3_stale_halo(const void* x, const void* halo_top, const void*
  * y is exactly what dp_conv3x3_stale_halo writes.  gn_sums[b, g, :] =
  * (sum y, sum y^2) of the stored (bf16) outputs of batch item b over the h*W
  * tokens and the Cout/G channels of group g, float32, accumulated per output
- * tile in the conv epilogue and folded in a fixed order (deterministic; equal
- * to dp_groupnorm_sums of y up to float32 rounding order).
+ * tile in the conv epilogue and folded in a fixed order by a second launch
+ * (deterministic; equal to dp_groupnorm_sums of y up to float32 rounding
+ * order).
  * gn_sums [B, G, 2] float32; ws/ws_bytes: caller-owned device scratch of at
- * least dp_conv3x3_gn_sums_workspace(B, h, W, Cout) bytes, zero-filled by the
- * caller before its first use (its first 32 KiB hold ticket counters that
- * every call leaves at zero again, so one zero fill serves any later calls
- * and shapes, on one stream at a time); other arguments as
- * dp_conv3x3_stale_halo.
+ * least dp_conv3x3_gn_sums_workspace(B, h, W, Cout) bytes for the tile
+ * partials; its contents on entry do not matter, and calls that share it
+ * must not overlap in time; other arguments as dp_conv3x3_stale_halo.
  * Supported: bf16 with Cin % 32 == 0, Cin <= 2048, Cout % 32 == 0,
  * Cout <= 2048 and h*W >= 160.  Errors: INVALID_ARG for NULL x/w/y/gn_sums, sizes <= 0,
  * Cout % G != 0, a short workspace or overlapping buffers; UNSUPPORTED

@@ -221,7 +221,7 @@ def test_conv_gn_sums_and_apply_validation(lib):
     f = lib.dp_conv3x3_stale_halo_gn_sums
     need = lib.dp_conv3x3_gn_sums_workspace(2, 30, 240, 640)
     # partials for the smallest tile shape (64x64: 225 x 10 tiles) and one
-    # channel per group (65 slots), two batch segments, plus the counters
+    # channel per group (65 slots), two batch segments
     assert need >= 225 * 2 * 10 * 65 * 8
     ok = [A, None, None, Bp, None, Cp, D, 32, E, need, 2, 30, 240, 640, 640, _lib.DP_BF16, None]
 
