@@ -133,6 +133,8 @@ def stale_sums_for(B, T_rem, C, G, N, seed, dt):
     ("bf16", 1, 17, 64, 8, 1, 0, False, False), ("f32", 2, 512, 64, 32, 2, 0, False, True),
     ("f32", 2, 100, 12, 4, 3, 2, True, False), ("bf16", 2, 64, 1280, 32, 2, 0, True, True),
     ("bf16", 1, 40, 1024, 1024, 2, 1, False, True),  # one channel per group
+    # 16 patches x 32 groups: more stale entries than apply threads, staged by the loop
+    ("bf16", 2, 300, 320, 32, 16, 5, True, True),
 ])
 def test_groupnorm(dt, B, T, C, G, N, rank, silu, affine):
     say("gn", dt, B, T, C, G, N, rank, silu, affine)
