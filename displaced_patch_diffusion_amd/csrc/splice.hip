@@ -14,8 +14,8 @@
 
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kUnroll = 4;
+constexpr int kThreads = 512;
+constexpr int kUnroll = 2;
 
 template <typename V>
 __global__ void __launch_bounds__(kThreads)
@@ -30,6 +30,15 @@ splice_kernel(char* __restrict__ k_buf, char* __restrict__ v_buf, const char* __
   const V* __restrict__ s = reinterpret_cast<const V*>(src);
   const int64_t base = static_cast<int64_t>(blockIdx.x) * (kThreads * kUnroll) + threadIdx.x;
   V tmp[kUnroll];
+  if (base + (kUnroll - 1) * kThreads < n_vec) {
+    // a whole block's worth: no per-load conditions, so both loads are in
+    // flight before the first store waits for its own
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) tmp[u] = __builtin_nontemporal_load(s + base + u * kThreads);
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) __builtin_nontemporal_store(tmp[u], d + base + u * kThreads);
+    return;
+  }
 #pragma unroll
   for (int u = 0; u < kUnroll; ++u) {
     const int64_t i = base + u * kThreads;
