@@ -510,37 +510,62 @@ __global__ void __launch_bounds__(256, 3) attn_bf16_d64(AttnArgs a) {
 }
 
 // Merges the key-chunk partials: o = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s.
-// One thread per (batch, query, head, 8-channel group).
+// Only the split units (n_whole on) are launched: four 256-thread blocks per
+// unit, one thread per (query row, 8-channel group), so the unit's (batch,
+// head, query block) is the same for the whole block.  SS > 0 compiles the
+// merge for exactly SS chunks with every load issued before the first is
+// used; SS = 0 loops over S chunks.  Both add in chunk order.
+constexpr int kCombineBlocksPerUnit = kBMq * 8 / 256;
+template <int SS>
 __global__ void __launch_bounds__(256)
 attn_combine(const float* __restrict__ part_o, const float* __restrict__ part_ml,
-             bf16_t* __restrict__ out, int B, int H, int Tq, int S, int n_whole) {
-  const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  const int64_t total = static_cast<int64_t>(B) * Tq * H * 8;
-  if (idx >= total) return;
-  const int ch = static_cast<int>(idx & 7);
-  int64_t r = idx >> 3;
-  const int h = static_cast<int>(r % H);
-  r /= H;
-  const int q = static_cast<int>(r % Tq);
-  const int b = static_cast<int>(r / Tq);
-  if ((static_cast<int64_t>(b) * H + h) * ((Tq + kBMq - 1) / kBMq) + q / kBMq < n_whole) return;  // written whole
+             bf16_t* __restrict__ out, int B, int H, int Tq, int S_arg, int n_whole, int n_qblk) {
+  const int u = n_whole + static_cast<int>(blockIdx.x) / kCombineBlocksPerUnit;
+  const int row = (static_cast<int>(blockIdx.x) % kCombineBlocksPerUnit) * (256 / 8) + static_cast<int>(threadIdx.x) / 8;
+  const int ch = static_cast<int>(threadIdx.x) & 7;
+  const int qb = u % n_qblk, bh = u / n_qblk, h = bh % H, b = bh / H;
+  const int q = qb * kBMq + row;
+  if (q >= Tq) return;
   const int C = H * kD;
-  float M = -INFINITY;
-  for (int s = 0; s < S; ++s)
-    M = fmaxf(M, part_ml[(((static_cast<int64_t>(s) * B + b) * H + h) * Tq + q) * 2]);
+  const int S = SS > 0 ? SS : S_arg;
+  auto ml_of = [&](int s) { return part_ml + (((static_cast<int64_t>(s) * B + b) * H + h) * Tq + q) * 2; };
+  auto o_of = [&](int s) { return part_o + ((static_cast<int64_t>(s) * B + b) * Tq + q) * C + h * kD + ch * 8; };
+  float M = -INFINITY, L = 0.f;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  float L = 0.f;
-  for (int s = 0; s < S; ++s) {
-    const float* ml = part_ml + (((static_cast<int64_t>(s) * B + b) * H + h) * Tq + q) * 2;
-    const float w = __builtin_amdgcn_exp2f(ml[0] - M);
-    L = fmaf(w, ml[1], L);
-    const float* po = part_o + ((static_cast<int64_t>(s) * B + b) * Tq + q) * C + h * kD + ch * 8;
-    const f32x4 x0 = *reinterpret_cast<const f32x4*>(po);
-    const f32x4 x1 = *reinterpret_cast<const f32x4*>(po + 4);
+  if constexpr (SS > 0) {
+    float2 ml[SS];
+    f32x4 x0[SS], x1[SS];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      acc[j] = fmaf(w, x0[j], acc[j]);
-      acc[4 + j] = fmaf(w, x1[j], acc[4 + j]);
+    for (int s = 0; s < SS; ++s) {
+      ml[s] = *reinterpret_cast<const float2*>(ml_of(s));
+      x0[s] = *reinterpret_cast<const f32x4*>(o_of(s));
+      x1[s] = *reinterpret_cast<const f32x4*>(o_of(s) + 4);
+    }
+#pragma unroll
+    for (int s = 0; s < SS; ++s) M = fmaxf(M, ml[s].x);
+#pragma unroll
+    for (int s = 0; s < SS; ++s) {
+      const float w = __builtin_amdgcn_exp2f(ml[s].x - M);
+      L = fmaf(w, ml[s].y, L);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        acc[j] = fmaf(w, x0[s][j], acc[j]);
+        acc[4 + j] = fmaf(w, x1[s][j], acc[4 + j]);
+      }
+    }
+  } else {
+    for (int s = 0; s < S; ++s) M = fmaxf(M, ml_of(s)[0]);
+    for (int s = 0; s < S; ++s) {
+      const float* ml = ml_of(s);
+      const float w = __builtin_amdgcn_exp2f(ml[0] - M);
+      L = fmaf(w, ml[1], L);
+      const f32x4 x0 = *reinterpret_cast<const f32x4*>(o_of(s));
+      const f32x4 x1 = *reinterpret_cast<const f32x4*>(o_of(s) + 4);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        acc[j] = fmaf(w, x0[j], acc[j]);
+        acc[4 + j] = fmaf(w, x1[j], acc[4 + j]);
+      }
     }
   }
   const float inv = 1.0f / L;
@@ -560,7 +585,8 @@ struct AttnPlan {
 
 // Merges the pieces of the units that the balanced schedule split between
 // positions.  One thread per (batch, query, head, 8-channel group); a unit
-// owned wholly by one position was written directly and is skipped.
+// owned wholly by one position was written directly and is skipped.  Pieces
+// are added in position order.
 __global__ void __launch_bounds__(256)
 attn_combine_sk(const float* __restrict__ part_o, const float* __restrict__ part_ml, bf16_t* __restrict__ out,
                 int B, int H, int Tq, int n_qblk, int n_tiles, long long work, int grid) {
@@ -578,6 +604,54 @@ attn_combine_sk(const float* __restrict__ part_o, const float* __restrict__ part
   const long long wf = u * n_tiles, wl = wf + n_tiles - 1;
   const long long p0 = sk_owner(wf, work, grid), p1 = sk_owner(wl, work, grid);
   if (p0 == p1) return;
+  constexpr int kPieces = 4;
+  if (p1 - p0 < kPieces) {
+    // Up to kPieces positions: each range start computed once, every load
+    // issued before the first is used (unused entries re-read piece 0, which
+    // always exists: position p0 holds the unit's first work item).
+    long long slot[kPieces];
+    bool use[kPieces];
+    long long s_lo = sk_start(p0, work, grid);
+#pragma unroll
+    for (int i = 0; i < kPieces; ++i) {
+      const long long p = p0 + i, s_hi = sk_start(p + 1, work, grid);
+      use[i] = p <= p1 && s_hi != s_lo;  // an empty range holds no piece
+      slot[i] = p * 2 + (i == 0 && s_lo < wf ? 1 : 0);
+      s_lo = s_hi;
+    }
+    float2 ml[kPieces];
+    f32x4 x0[kPieces], x1[kPieces];
+#pragma unroll
+    for (int i = 0; i < kPieces; ++i) {
+      const long long sl = use[i] ? slot[i] : slot[0];
+      ml[i] = *reinterpret_cast<const float2*>(part_ml + (sl * kBMq + row) * 2);
+      const float* po = part_o + (sl * kBMq + row) * kD + ch * 8;
+      x0[i] = *reinterpret_cast<const f32x4*>(po);
+      x1[i] = *reinterpret_cast<const f32x4*>(po + 4);
+    }
+    float M = -INFINITY, L = 0.f;
+#pragma unroll
+    for (int i = 0; i < kPieces; ++i)
+      if (use[i]) M = fmaxf(M, ml[i].x);
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < kPieces; ++i) {
+      if (!use[i]) continue;
+      const float w = __builtin_amdgcn_exp2f(ml[i].x - M);
+      L = fmaf(w, ml[i].y, L);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        acc[j] = fmaf(w, x0[i][j], acc[j]);
+        acc[4 + j] = fmaf(w, x1[i][j], acc[4 + j]);
+      }
+    }
+    const float inv = 1.0f / L;
+    u32x4 pk;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) pk[j] = pack_bf16x2(acc[2 * j] * inv, acc[2 * j + 1] * inv);
+    *reinterpret_cast<u32x4*>(out + (static_cast<int64_t>(b) * Tq + q) * H * kD + h * kD + ch * 8) = pk;
+    return;
+  }
   float M = -INFINITY;
   for (long long p = p0; p <= p1; ++p) {
     if (sk_start(p + 1, work, grid) == sk_start(p, work, grid)) continue;  // empty range
@@ -877,10 +951,26 @@ DP_API dp_status dp_attn_stale_kv(const void* q, const void* k_buf, const void* 
                          stream, args.part_o, args.part_ml, args.out, (int)B, (int)H, (int)Tq, p.n_qblk,
                          p.n_tiles, p.work, p.grid);
     } else if (p.n_split > 1) {
-      const int64_t threads = B * Tq * H * 8;
-      hipLaunchKernelGGL(attn_combine, dim3(static_cast<unsigned>((threads + 255) / 256)), dim3(256), 0,
-                         stream, args.part_o, args.part_ml, args.out, (int)B, (int)H, (int)Tq, p.n_split,
-                         p.n_whole);
+      const int64_t split_units = B * H * p.n_qblk - p.n_whole;
+      const dim3 grid(static_cast<unsigned>(split_units * kCombineBlocksPerUnit));
+      switch (p.n_split) {
+        case 2:
+          hipLaunchKernelGGL(attn_combine<2>, grid, dim3(256), 0, stream, args.part_o, args.part_ml, args.out, (int)B,
+                             (int)H, (int)Tq, p.n_split, p.n_whole, p.n_qblk);
+          break;
+        case 3:
+          hipLaunchKernelGGL(attn_combine<3>, grid, dim3(256), 0, stream, args.part_o, args.part_ml, args.out, (int)B,
+                             (int)H, (int)Tq, p.n_split, p.n_whole, p.n_qblk);
+          break;
+        case 4:
+          hipLaunchKernelGGL(attn_combine<4>, grid, dim3(256), 0, stream, args.part_o, args.part_ml, args.out, (int)B,
+                             (int)H, (int)Tq, p.n_split, p.n_whole, p.n_qblk);
+          break;
+        default:
+          hipLaunchKernelGGL(attn_combine<0>, grid, dim3(256), 0, stream, args.part_o, args.part_ml, args.out, (int)B,
+                             (int)H, (int)Tq, p.n_split, p.n_whole, p.n_qblk);
+          break;
+      }
     }
   } else {
     const dim3 grid(static_cast<unsigned>((Tq + kFQ - 1) / kFQ), static_cast<unsigned>(H),
